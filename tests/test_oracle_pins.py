@@ -1,0 +1,349 @@
+"""Pins for the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names the fact it checks; none calls GPU code.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (INT32_MAX, attend_unit, bf16_round, build_slice, dense_unit, level_counts,
+                    plan_counts, rope_table, rotate)
+from brute64 import brute_unit, dense_textbook, rot as rot64
+from synthetic import bf16_bits, bf16_value
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rand(rng, shape, std=1.0, dtype="f32"):
+    x = (rng.standard_normal(shape) * std).astype(np.float32)
+    return bf16_value(bf16_bits(x)) if dtype == "bf16" else x
+
+
+# ------------------------------------------------------------------ rounding
+
+def test_bf16_round_is_torch_rne():
+    """bf16 rounding equals torch's float32 -> bfloat16 conversion (round to nearest, ties to even)."""
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(200_000) * 10.0 ** rng.integers(-8, 8, 200_000)).astype(np.float32)
+    ties = ((rng.integers(0, 1 << 15, 20_000).astype(np.uint32) << 16) | 0x8000).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    x = np.concatenate([x, ties, np.float32([0.0, -0.0, 1.0, -1.0])])
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(bf16_round(x).view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ brute force on tiny trees
+
+def _brute_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    f = int(rng.choice([2, 3, 4, 16]))
+    d = int(rng.choice([8, 16, 64]))
+    G = int(rng.choice([1, 4]))
+    theta = float(rng.choice([0.0, 1.0e6, 50.0]))
+    self_in = bool(rng.integers(0, 2))
+    n_max = 5000 if f == 16 else 520
+    n = int(rng.integers(1 if self_in else 0, n_max))
+    T = len(level_counts(n, f))
+    k = [int(rng.integers(0, f + 2)) for _ in range(T + 1)]
+    if rng.random() < 0.15 and T:
+        k[int(rng.integers(0, T))] = INT32_MAX
+    K = _rand(rng, (max(n, 1), d))
+    V = _rand(rng, (max(n, 1), d))
+    q = _rand(rng, (G, d))
+    W = (np.eye(d) + 0.3 / np.sqrt(d) * rng.standard_normal((d, d))).astype(np.float32)
+    return f, d, G, theta, self_in, n, k, K, V, q, W
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_oracle_matches_float64_brute_force(seed):
+    """Whole algorithm (f32 storage) vs an independent float64 formulation on tiny inputs:
+    selections equal level by level unless either side sees a near tie; outputs within 1e-6."""
+    f, d, G, theta, self_in, n, k, K, V, q, W = _brute_case(seed)
+    tree = build_slice(K, V, W, f, "f32", n_new=n)
+    r = attend_unit(q, K, V, tree, n, f, k, "f32", theta, self_in=self_in)
+    b = brute_unit(q, K, V, W, n, f, k, theta, self_in=self_in)
+    T = len(level_counts(n, f))
+    for lv in range(T, 0, -1):
+        if r.flags.get(lv) or b["gap"].get(lv, 1.0) < 1e-5:
+            pytest.skip(f"near tie at level {lv}: later levels are not comparable")
+        assert r.sel[lv] == b["sel"][lv], f"level {lv}"
+    assert sorted(r.entries) == sorted(b["entries"])
+    np.testing.assert_allclose(r.out, b["out"], rtol=0, atol=1e-6)
+    np.testing.assert_allclose(r.lse, b["lse"], rtol=0, atol=1e-6)
+
+
+def test_brute_force_cases_mostly_compared():
+    """Guard against the comparison above skipping everything."""
+    skipped = 0
+    for seed in range(48):
+        f, d, G, theta, self_in, n, k, K, V, q, W = _brute_case(seed)
+        tree = build_slice(K, V, W, f, "f32", n_new=n)
+        r = attend_unit(q, K, V, tree, n, f, k, "f32", theta, self_in=self_in)
+        skipped += any(r.flags.values())
+    assert skipped <= 8
+
+
+# ------------------------------------------------------------------ no pruning = dense RoPE attention
+
+@pytest.mark.parametrize("dtype,tol", [("f32", 1e-6), ("bf16", 2e-3)])
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+@pytest.mark.parametrize("f", [2, 4, 16])
+def test_no_pruning_equals_textbook_dense(dtype, tol, mode, f):
+    """k >= C at every level keeps every node, so every token is an exact entry at its own
+    position and the query sits at n (decode) or t (prefill): textbook RoPE attention."""
+    rng = np.random.default_rng(7 + f)
+    d, G, n = 64, 4, 300
+    std = 1.0 if dtype == "f32" else d ** -0.5
+    K, V = _rand(rng, (n, d), std, dtype), _rand(rng, (n, d), std, dtype)
+    q = _rand(rng, (G, d), std, dtype)
+    W = _rand(rng, (d, d), 0.1, dtype)
+    theta = 1.0e4
+    tree = build_slice(K, V, W, f, dtype, n_new=n)
+    k = [INT32_MAX] * 10
+    r = attend_unit(q, K, V, tree, n, f, k, dtype, theta, self_in=(mode == "prefill"))
+    assert all(lv == 0 for lv, _ in r.entries) and len(r.entries) == n
+    q_pos = n if mode == "decode" else n - 1
+    out, lse = dense_textbook(q, K, V, n, q_pos, theta)
+    np.testing.assert_allclose(r.out, out, rtol=0, atol=tol)
+    np.testing.assert_allclose(r.lse, lse, rtol=0, atol=10 * tol)
+    do, dl = dense_unit(q, K, V, n, q_pos, dtype, theta)
+    np.testing.assert_allclose(r.out, do, rtol=0, atol=1e-12)
+
+
+def test_dense_oracle_matches_textbook_long_positions():
+    """The dense comparator at positions near 2M (f32): rotation angles far beyond 2*pi."""
+    rng = np.random.default_rng(3)
+    d, G, n = 64, 4, 2100
+    K, V, q = _rand(rng, (n, d)), _rand(rng, (n, d)), _rand(rng, (G, d))
+    # shift positions by building the key array at the end of a long virtual cache
+    theta = 1.0e6
+    out, lse = dense_unit(q, K, V, n, n, "f32", theta)
+    ref, rlse = dense_textbook(q, K, V, n, n, theta)
+    np.testing.assert_allclose(out, ref, atol=1e-6, rtol=0)
+    np.testing.assert_allclose(lse, rlse, atol=1e-5, rtol=0)
+
+
+# ------------------------------------------------------------------ closed forms
+
+def test_fewer_tokens_than_fanout_is_dense():
+    rng = np.random.default_rng(11)
+    d, G, f = 16, 4, 16
+    for n in range(0, f):
+        K, V, q = _rand(rng, (max(n, 1), d)), _rand(rng, (max(n, 1), d)), _rand(rng, (G, d))
+        tree = build_slice(K, V, np.eye(d, dtype=np.float32), f, "f32", n_new=n)
+        r = attend_unit(q, K, V, tree, n, f, [0], "f32", 1e6)
+        assert r.entries == [(0, t) for t in range(n)]
+        if n:
+            ref, rl = dense_textbook(q, K, V, n, n, 1e6)
+            np.testing.assert_allclose(r.out, ref, atol=1e-6, rtol=0)
+        else:
+            assert np.all(r.out == 0) and np.all(np.isneginf(r.lse))
+
+
+def test_single_unkept_node_returns_its_mean_value():
+    """n = f with k_1 = 0: the only entry is the root summary, so out = mean of V exactly as stored."""
+    rng = np.random.default_rng(12)
+    d, G, f = 32, 4, 8
+    K, V, q = _rand(rng, (f, d)), _rand(rng, (f, d)), _rand(rng, (G, d))
+    tree = build_slice(K, V, np.eye(d, dtype=np.float32), f, "f32", n_new=f)
+    r = attend_unit(q, K, V, tree, f, f, [0], "f32", 1e6)
+    assert r.entries == [(1, 0)]
+    np.testing.assert_allclose(r.out, np.repeat(V.astype(np.float64).mean(0)[None], G, 0), atol=1e-7, rtol=0)
+    np.testing.assert_array_equal(r.out, np.repeat(tree[0][1][0:1].astype(np.float64), G, 0))
+
+
+@pytest.mark.parametrize("f,T,m", [(4, 3, 3), (16, 2, 5), (2, 6, 1)])
+def test_top_level_only_is_library_attention(f, T, m):
+    """k_T = 0 on n = m f^T tokens: the softmax covers exactly the m top-level summaries, keys
+    rotated at 0..m-1 and the query at m -- torch's scaled_dot_product_attention in float64."""
+    rng = np.random.default_rng(20 + f)
+    d, G = 32, 4
+    n = m * f ** T
+    K, V, q = _rand(rng, (n, d)), _rand(rng, (n, d)), _rand(rng, (G, d))
+    W = (np.eye(d) + 0.2 * rng.standard_normal((d, d)) / np.sqrt(d)).astype(np.float32)
+    theta = 100.0
+    tree = build_slice(K, V, W, f, "f32", n_new=n)
+    k = [5] * (T - 1) + [0]
+    r = attend_unit(q, K, V, tree, n, f, k, "f32", theta)
+    assert r.entries == [(T, g) for g in range(m)]
+    NK, NV = tree[T - 1]
+    Kr = np.stack([rot64(NK[g].astype(np.float64), g, theta) for g in range(m)])
+    Qr = np.stack([rot64(q[h].astype(np.float64), m, theta) for h in range(G)])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Qr)[None, :, None, :], torch.from_numpy(Kr)[None, None].expand(1, G, m, d),
+        torch.from_numpy(NV.astype(np.float64))[None, None].expand(1, G, m, d), scale=1.0 / np.sqrt(d))
+    np.testing.assert_allclose(r.out, ref[0, :, 0].numpy(), atol=1e-6, rtol=0)
+
+
+@pytest.mark.parametrize("f,n,k", [(16, 4096, [4, 4, 4]), (4, 777, [1, 0, 3, 2, 9]), (3, 500, [7, 2, 2, 1, 1, 0])])
+def test_zero_keys_select_lowest_indices(f, n, k):
+    """K = 0 makes every logit exactly 0: the kept nodes are the first s_l candidates (lowest
+    index wins ties), the weights are uniform and lse = log(E)."""
+    rng = np.random.default_rng(5)
+    d, G = 16, 4
+    K = np.zeros((n, d), np.float32)
+    V, q = _rand(rng, (n, d)), _rand(rng, (G, d))
+    W = _rand(rng, (d, d))
+    tree = build_slice(K, V, W, f, "f32", n_new=n)
+    r = attend_unit(q, K, V, tree, n, f, k, "f32", 1e6)
+    nl = level_counts(n, f)
+    T = len(nl)
+    prev_s, n_up = 0, 0
+    for lv in range(T, 0, -1):
+        kids = f * prev_s                      # the kept nodes one level up are 0..prev_s-1
+        orph = list(range(f * n_up, nl[lv - 1]))
+        cand = list(range(kids)) + orph
+        s = min(k[lv - 1], len(cand))
+        assert r.sel[lv] == cand[:s], lv
+        prev_s, n_up = s, nl[lv - 1]
+        assert r.sel[lv] == list(range(s)) or s > kids
+    E = len(r.entries)
+    np.testing.assert_allclose(r.lse, np.log(E), rtol=0, atol=1e-12)
+    vals = []
+    for lv, i in r.entries:
+        vals.append(V[i] if lv == 0 else tree[lv - 1][1][i])
+    np.testing.assert_allclose(r.out, np.repeat(np.mean(np.array(vals, np.float64), 0)[None], G, 0),
+                               atol=1e-12, rtol=0)
+
+
+# ------------------------------------------------------------------ tree build
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_node_summaries_are_subtree_means(dtype):
+    """Node value = mean of its subtree's token values; with W = I the node key is the mean of
+    its subtree's keys; in general the key is W^l applied to that mean (the pooler is linear)."""
+    rng = np.random.default_rng(9)
+    f, d, n = 4, 16, 4 ** 5
+    K, V = _rand(rng, (n, d), 1.0, dtype), _rand(rng, (n, d), 1.0, dtype)
+    W = _rand(rng, (d, d), 0.5 / np.sqrt(d), dtype) + np.eye(d, dtype=np.float32)
+    if dtype == "bf16":
+        W = bf16_value(bf16_bits(W))
+    eye = np.eye(d, dtype=np.float32)
+    tr_I = build_slice(K, V, eye, f, dtype, n_new=n)
+    tr_W = build_slice(K, V, W, f, dtype, n_new=n)
+    for lv, cnt in enumerate(level_counts(n, f), start=1):
+        span = f ** lv
+        tok_mean_V = V.astype(np.float64).reshape(cnt, span, d).mean(1)
+        tok_mean_K = K.astype(np.float64).reshape(cnt, span, d).mean(1)
+        tol = 2e-6 * lv if dtype == "f32" else lv * 2.0 ** -8
+        scaleV = np.abs(V).max()
+        assert np.abs(tr_I[lv - 1][1] - tok_mean_V).max() <= tol * scaleV
+        assert np.abs(tr_I[lv - 1][0] - tok_mean_K).max() <= tol * np.abs(K).max()
+        ref = tok_mean_K @ np.linalg.matrix_power(W.astype(np.float64), lv).T
+        assert np.abs(tr_W[lv - 1][0] - ref).max() <= 4 * tol * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_incremental_build_is_bitwise_one_shot(dtype):
+    rng = np.random.default_rng(10)
+    f, d, n = 4, 8, 1000
+    K, V = _rand(rng, (n, d), 1.0, dtype), _rand(rng, (n, d), 1.0, dtype)
+    W = bf16_value(bf16_bits(_rand(rng, (d, d)))) if dtype == "bf16" else _rand(rng, (d, d))
+    one = build_slice(K, V, W, f, dtype, n_new=n)
+    cuts = sorted(set(rng.integers(0, n, 12).tolist() + [0, n]))
+    tree = None
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        tree = build_slice(K, V, W, f, dtype, n_new=b, n_old=a, tree=tree, cap=n)
+    for (k1, v1), (k2, v2) in zip(one, tree):
+        assert np.array_equal(k1.view(np.uint32), k2.view(np.uint32))
+        assert np.array_equal(v1.view(np.uint32), v2.view(np.uint32))
+
+
+# ------------------------------------------------------------------ structure
+
+@pytest.mark.parametrize("seed", range(12))
+def test_entries_partition_the_prefix(seed):
+    """Every token is covered exactly once, by itself or by the summary that replaced it;
+    E = sum(C_l - s_l) + C_0; C_l <= f s_{l+1} + f - 1; weights sum to 1; counts follow the closed form."""
+    rng = np.random.default_rng(50 + seed)
+    f = int(rng.choice([2, 3, 8, 16]))
+    n = int(rng.integers(1, 20000))
+    d, G = 8, 2
+    K, V, q = _rand(rng, (n, d)), _rand(rng, (n, d)), _rand(rng, (G, d))
+    T = len(level_counts(n, f))
+    k = [int(rng.integers(0, 2 * f)) for _ in range(T)]
+    self_in = bool(seed % 2)
+    tree = build_slice(K, V, np.eye(d, dtype=np.float32), f, "f32", n_new=n)
+    r = attend_unit(q, K, V, tree, n, f, k, "f32", 1e6, self_in=self_in)
+    cover = np.zeros(n, np.int64)
+    for lv, i in r.entries:
+        cover[i * f ** lv:(i + 1) * f ** lv] += 1
+    assert np.all(cover == 1)
+    C, s, C0 = plan_counts(n, f, k)
+    assert {lv: r.C[lv] for lv in C} == C and r.C[0] == C0
+    assert len(r.entries) == sum(C[lv] - s[lv] for lv in C) + C0
+    for lv in C:
+        assert C[lv] <= f * (s.get(lv + 1, 0)) + f - 1
+        assert len(r.sel[lv]) == s[lv]
+    np.testing.assert_allclose(r.weights.sum(0), 1.0, atol=1e-12)
+
+
+def test_counts_match_hand_derived_table():
+    with open(os.path.join(HERE, "golden", "counts_aligned.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        T = len(level_counts(c["n"], c["f"]))
+        C, s, C0 = plan_counts(c["n"], c["f"], [c["k"]] * T)
+        assert {str(k): v for k, v in C.items()} == c["C"], c["name"]
+        assert {str(k): v for k, v in s.items()} == c["s"], c["name"]
+        assert C0 == c["C0"]
+        assert sum(C[lv] - s[lv] for lv in C) + C0 == c["E"]
+
+
+# ------------------------------------------------------------------ RoPE
+
+def test_rotation_properties():
+    """Rotation preserves norms, is the identity at position 0, logits depend only on the
+    position difference, and rotate-half equals the complex-pair form."""
+    rng = np.random.default_rng(4)
+    d = 64
+    c, s = rope_table(5100, d, 1.0e6)
+    x = _rand(rng, (50, d))
+    assert np.array_equal(rotate(x, c[0][None], s[0][None], "f32"), x)
+    pos = rng.integers(0, 4000, 50)
+    r = rotate(x, c[pos], s[pos], "f32").astype(np.float64)
+    np.testing.assert_allclose(np.linalg.norm(r, axis=1), np.linalg.norm(x.astype(np.float64), axis=1), rtol=1e-6)
+    ref = np.stack([rot64(x[i].astype(np.float64), int(pos[i]), 1.0e6) for i in range(50)])
+    np.testing.assert_allclose(r, ref, atol=2e-6, rtol=0)
+    y = _rand(rng, (50, d))
+    for sh in (1, 17, 1000):
+        a = (rotate(x, c[pos], s[pos], "f32").astype(np.float64) *
+             rotate(y, c[pos // 2], s[pos // 2], "f32").astype(np.float64)).sum(1)
+        b = (rotate(x, c[pos + sh], s[pos + sh], "f32").astype(np.float64) *
+             rotate(y, c[pos // 2 + sh], s[pos // 2 + sh], "f32").astype(np.float64)).sum(1)
+        np.testing.assert_allclose(a, b, atol=1e-4, rtol=0)
+
+
+# ------------------------------------------------------------------ planted needles
+
+def test_planted_needles_are_exact_entries():
+    """No RoPE, W = I. Background keys are orthogonal to every test query head; the query heads
+    of different targets are mutually orthogonal; each target has needles along its summed
+    query direction. Only the needles' ancestors score above zero for their target, so each
+    target keeps every one of its needles as an exact token (at most k per target)."""
+    rng = np.random.default_rng(77)
+    d, G, f, n, k = 64, 4, 16, 4096, 4
+    n_targets = 4
+    U, _ = np.linalg.qr(rng.standard_normal((d, n_targets * G)))
+    U = U.T                                                   # orthonormal rows
+    K = rng.standard_normal((n, d))
+    K -= (K @ U.T) @ U
+    V = rng.standard_normal((n, d))
+    plan = {}
+    for j in range(n_targets):
+        u = U[j * G:(j + 1) * G].sum(0)
+        u /= np.linalg.norm(u)
+        pos = rng.choice(n, size=2, replace=False)
+        plan[j] = sorted(int(p) for p in pos)
+        for p in pos:
+            K[p] = 3.0 * 8.0 * u
+    K, V = K.astype(np.float32), V.astype(np.float32)
+    tree = build_slice(K, V, np.eye(d, dtype=np.float32), f, "f32", n_new=n)
+    for j in range(n_targets):
+        q = (4.0 * U[j * G:(j + 1) * G]).astype(np.float32)
+        r = attend_unit(q, K, V, tree, n, f, [k] * 3, "f32", 0.0)
+        toks = {i for lv, i in r.entries if lv == 0}
+        assert set(plan[j]) <= toks, (j, plan[j])
