@@ -1,0 +1,173 @@
+/*
+ * recsa.h -- RecSA tree attention on AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * Method, cited by page title and section:
+ *   [Abstract]  "Recursive Sparse Attention: Million-Token Length Extrapolation
+ *               at Logarithmic Cost", abstract.
+ *   [Core Idea] "Recursive Sparse Attention RecSA: Million-Token Context
+ *               Extrapolation at Logarithmic Cost", section "Core Idea:
+ *               Compressing the KV Cache with a Tree Structure".
+ *   [Position]  the same page, section "Position Encoding Ingenuity: Making
+ *               Extrapolation Possible".
+ *
+ * A tree is kept over each (sequence, KV head) of the KV cache. A node at
+ * level l >= 1 covers f^l consecutive tokens and exists once all f children
+ * exist; it holds one pooled key, W @ (mean of its children's stored keys),
+ * and one value, the mean of its children's stored values [Abstract, Core
+ * Idea]. A query descends from the top level; at each level its candidates
+ * are the children of the nodes it kept one level up, followed by the nodes
+ * that have no complete parent; it keeps the min(k_l, C_l) candidates with
+ * the highest score (the scaled RoPE logit summed over the query heads that
+ * share the KV head, ties to the lower candidate index) [Abstract]. Every
+ * candidate's key is rotated at its index among its level's candidates and
+ * the query at C_l [Abstract, Position]; at the token level the candidates are
+ * the tokens under the kept level-1 nodes plus the trailing partial block,
+ * and the query sits at C_0, or C_0 - 1 when its own token is a candidate.
+ * The candidates not kept, each with its node's mean value, and the
+ * token-level candidates share one softmax per query head [Abstract].
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked [dev] are caller-owned HIP device memory; [host] are
+ *     host memory read during the call only. The library never frees caller
+ *     memory and allocates no device memory.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls validate all
+ *     arguments on the host first, then enqueue kernels on `stream` and return
+ *     without waiting; outputs are valid once the stream reaches that point.
+ *   - Storage type `dtype` (RECSA_F32 or RECSA_BF16) applies to K, V, q, the
+ *     pooler W and the tree nodes. Outputs are float32.
+ *   - Arrays are dense, row-major, with the innermost dimension head_dim;
+ *     device pointers must be 16-byte aligned.
+ *   - Every argument error is reported before any launch, as a negative
+ *     status; recsa_last_error() then returns a message (thread-local). A
+ *     failed HIP launch returns RECSA_ERR_HIP. No exceptions cross the ABI.
+ *   - Calls on distinct streams with distinct output buffers may run
+ *     concurrently; a workspace must not be shared by calls in flight.
+ */
+#ifndef RECSA_H
+#define RECSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RECSA_ABI_VERSION 1
+#define RECSA_MAX_LEVELS 32
+
+typedef enum {
+  RECSA_OK = 0,
+  RECSA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned pointer, k < 0, ... */
+  RECSA_ERR_CAPACITY = -2,     /* token count beyond the cache capacity */
+  RECSA_ERR_UNSUPPORTED = -3,  /* shape outside what the kernels are built for */
+  RECSA_ERR_HIP = -4,          /* a HIP runtime call or launch failed */
+  RECSA_ERR_WORKSPACE = -5     /* workspace smaller than required */
+} recsa_status_t;
+
+typedef enum { RECSA_F32 = 0, RECSA_BF16 = 1 } recsa_dtype_t;
+
+typedef struct {
+  int32_t batch;          /* B sequences */
+  int32_t n_kv_heads;     /* H_kv */
+  int32_t n_q_heads;      /* H_q, a multiple of H_kv; G = H_q / H_kv query heads share a KV head (G <= 8) */
+  int32_t head_dim;       /* d: 64 or 128 */
+  int32_t fanout;         /* f: 2..64 */
+  int32_t dtype;          /* recsa_dtype_t */
+  int64_t capacity;       /* tokens per (sequence, KV head) slice of K and V; sizes the tree */
+  float softmax_scale;    /* 0 => 1/sqrt(d), rounded to float32 */
+  float rope_theta;       /* RoPE base (1e6 for Qwen3-style models); 0 disables the rotation */
+} recsa_shape_t;
+
+/* ABI version (RECSA_ABI_VERSION). */
+int32_t recsa_abi_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* recsa_last_error(void);
+
+/* T = max{l : floor(n / f^l) >= 1}, 0 when n < f (the complete-node forest). */
+int32_t recsa_num_levels(int64_t n_tokens, int32_t fanout);
+
+/* Bytes of the tree buffer for `capacity` tokens: for l = 1..T(capacity), the node keys
+ * NK_l [B][H_kv][floor(capacity/f^l)][d] followed by the node values NV_l of the same shape,
+ * level after level, in the storage type. Returns -1 on an invalid shape. */
+int64_t recsa_tree_bytes(const recsa_shape_t* shape);
+
+/* Byte offset of NK_l (which = 0) or NV_l (which = 1) inside the tree buffer; -1 if invalid. */
+int64_t recsa_level_offset(const recsa_shape_t* shape, int32_t level, int32_t which);
+
+/* Columns the `sel` output needs: the largest number of nodes kept at any level by any query
+ * whose visible prefix has between n_min and n_max tokens. -1 if invalid. */
+int32_t recsa_sel_width(const recsa_shape_t* shape, int64_t n_min, int64_t n_max,
+                        const int32_t* k_per_level /*[host] n_levels*/, int32_t n_levels);
+
+/* Workspace bytes needed by recsa_decode / recsa_prefill for visible prefixes of up to
+ * n_max tokens, or by recsa_dense_ref_attn (k_per_level = NULL) for positions up to n_max.
+ * -1 if invalid. */
+int64_t recsa_workspace_bytes(const recsa_shape_t* shape, int64_t n_max,
+                              const int32_t* k_per_level /*[host] or NULL*/, int32_t n_levels);
+
+/* Step 1, tree build [Abstract, Core Idea].
+ * Builds every node that is complete at n_new tokens but not at n_old, bottom level first:
+ *   m = (sum of the f children's stored keys, in child order, float32) / f
+ *   NK = round(W @ m)      (each output accumulated input by input, float32, no fused multiply-add)
+ *   NV = round((sum of the f children's stored values, in child order, float32) / f)
+ * Children are token rows at level 1 and stored level-(l-1) nodes above. Nodes complete at
+ * n_old are left untouched, so growing the cache in any number of steps gives the same tree.
+ *   K, V [dev]: [B][H_kv][capacity][d] pre-RoPE; W [dev]: [d][d] (key_i = sum_j W[i][j] m_j);
+ *   tree [dev]: recsa_tree_bytes(shape) bytes.
+ * Errors: INVALID_ARG (null, misaligned, n_old > n_new, n_old < 0), CAPACITY (n_new > capacity),
+ * UNSUPPORTED (d, f or dtype). */
+int32_t recsa_build_tree(const recsa_shape_t* shape, const void* K, const void* V, const void* W,
+                         int64_t n_old, int64_t n_new, void* tree, void* stream);
+
+/* Steps 2-4 for decoding [Abstract]: n_q queries per sequence, all at position n_tokens and
+ * not in the cache, against the first n_tokens cached tokens (the tree must hold every node
+ * complete at n_tokens).
+ *   q [dev]: [B][n_q][H_q][d]; k_per_level [host]: k_l for l = 1..n_levels (n_levels >= T(n_tokens),
+ *   k_l >= 0, INT32_MAX = keep everything).
+ *   out [dev]: float32 [B][n_q][H_q][d]; lse [dev] (nullable): float32 [B][n_q][H_q], log of the
+ *   softmax denominator (-inf and out = 0 when there is no entry, i.e. n_tokens = 0).
+ *   sel [dev] (nullable): int32 [B][n_q][H_kv][n_levels][sel_width], the kept node ids of level
+ *   l in row l-1, ascending, padded with -1; sel_width >= recsa_sel_width(n_tokens, n_tokens).
+ *   workspace [dev]: ws_bytes >= recsa_workspace_bytes(shape, n_tokens, k, n_levels).
+ * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED (candidate lists too long for on-chip memory),
+ * WORKSPACE. */
+int32_t recsa_decode(const recsa_shape_t* shape, const void* q, int64_t n_q,
+                     const void* K, const void* V, const void* tree, int64_t n_tokens,
+                     const int32_t* k_per_level, int32_t n_levels,
+                     float* out, float* lse, int32_t* sel, int32_t sel_width,
+                     void* workspace, int64_t ws_bytes, void* stream);
+
+/* Steps 2-4 for causal prefill [Abstract]: query j sits at position t = q_start + j and sees
+ * tokens 0..t, its own token included, through the nodes complete at t + 1 (the tree must hold
+ * every node complete at q_start + n_q; nodes beyond a query's prefix are ignored). The result
+ * does not depend on how a caller splits positions into calls.
+ *   q [dev]: [B][n_q][H_q][d]; out float32 [B][n_q][H_q][d]; lse [B][n_q][H_q] (nullable);
+ *   sel [B][n_q][H_kv][n_levels][sel_width] (nullable),
+ *   sel_width >= recsa_sel_width(q_start + 1, q_start + n_q).
+ *   workspace: recsa_workspace_bytes(shape, q_start + n_q, k, n_levels).
+ * Errors as recsa_decode. */
+int32_t recsa_prefill(const recsa_shape_t* shape, const void* q, int64_t q_start, int64_t n_q,
+                      const void* K, const void* V, const void* tree,
+                      const int32_t* k_per_level, int32_t n_levels,
+                      float* out, float* lse, int32_t* sel, int32_t sel_width,
+                      void* workspace, int64_t ws_bytes, void* stream);
+
+/* Dense softmax attention with standard RoPE at the original positions -- the comparator the
+ * method is timed against [Abstract]; also RecSA's limit when every level keeps everything.
+ *   causal = 0: decode, every query at position n_tokens against keys 0..n_tokens-1
+ *   (q_start ignored). causal = 1: query j at position t = q_start + j against keys 0..t
+ *   (q_start + n_q <= n_tokens).
+ *   q [dev]: [B][n_q][H_q][d]; out float32 [B][n_q][H_q][d]; lse float32 [B][n_q][H_q] (nullable).
+ *   workspace: recsa_workspace_bytes(shape, n_tokens, NULL, 0).
+ * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED, WORKSPACE. */
+int32_t recsa_dense_ref_attn(const recsa_shape_t* shape, const void* q, int64_t q_start, int64_t n_q,
+                             const void* K, const void* V, int64_t n_tokens, int32_t causal,
+                             float* out, float* lse, void* workspace, int64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RECSA_H */

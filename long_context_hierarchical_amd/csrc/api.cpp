@@ -1,0 +1,360 @@
+// RecSA C ABI: argument validation, tree layout, workspace sizing and launch order.
+// Every entry point validates everything before the first launch and reports errors
+// as negative status codes with a thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+#include "recsa.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+  return fail(RECSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxList = 4096;     // kept-node / candidate list capacity in LDS
+constexpr size_t kMaxLds = 65536;
+constexpr int64_t kTableAlign = 256;
+
+struct Info {
+  int64_t B, Hkv, Hq, d, f, G, cap;
+  bool bf16;
+  int64_t esz;
+  float scale, theta;
+};
+
+int32_t check_shape(const recsa_shape_t* s, Info* o) {
+  if (!s) return fail(RECSA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch <= 0 || s->n_kv_heads <= 0 || s->n_q_heads <= 0)
+    return fail(RECSA_ERR_INVALID_ARG, "batch, n_kv_heads and n_q_heads must be positive");
+  if (s->n_q_heads % s->n_kv_heads != 0)
+    return fail(RECSA_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", s->n_q_heads,
+                s->n_kv_heads);
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(RECSA_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", G);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(RECSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", s->head_dim);
+  if (s->fanout < 2 || s->fanout > 64) return fail(RECSA_ERR_UNSUPPORTED, "fanout must be in 2..64 (got %d)", s->fanout);
+  if (s->dtype != RECSA_F32 && s->dtype != RECSA_BF16) return fail(RECSA_ERR_UNSUPPORTED, "dtype %d", s->dtype);
+  if (s->capacity < 0 || s->capacity > INT32_MAX)
+    return fail(RECSA_ERR_INVALID_ARG, "capacity must be in 0..2^31-1");
+  if (!(s->softmax_scale >= 0.0f) || !std::isfinite(s->softmax_scale))
+    return fail(RECSA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (!(s->rope_theta >= 0.0f) || !std::isfinite(s->rope_theta) || (s->rope_theta > 0.0f && s->rope_theta <= 1.0f))
+    return fail(RECSA_ERR_INVALID_ARG, "rope_theta must be 0 or > 1");
+  o->B = s->batch;
+  o->Hkv = s->n_kv_heads;
+  o->Hq = s->n_q_heads;
+  o->d = s->head_dim;
+  o->f = s->fanout;
+  o->G = G;
+  o->cap = s->capacity;
+  o->bf16 = s->dtype == RECSA_BF16;
+  o->esz = o->bf16 ? 2 : 4;
+  o->scale = s->softmax_scale > 0.0f ? s->softmax_scale : static_cast<float>(1.0 / std::sqrt(static_cast<double>(s->head_dim)));
+  o->theta = s->rope_theta;
+  return RECSA_OK;
+}
+
+int levels_of(int64_t n, int64_t f) {
+  int T = 0;
+  for (int64_t m = n / f; m >= 1; m /= f) ++T;
+  return T;
+}
+
+int64_t nodes_at(int64_t n, int64_t f, int lv) {
+  int64_t m = n;
+  for (int i = 0; i < lv; ++i) m /= f;
+  return m;
+}
+
+int64_t level_offset_bytes(const Info& I, int lv, int which) {
+  int64_t off = 0;
+  for (int l = 1; l < lv; ++l) off += 2 * I.B * I.Hkv * nodes_at(I.cap, I.f, l) * I.d * I.esz;
+  if (which) off += I.B * I.Hkv * nodes_at(I.cap, I.f, lv) * I.d * I.esz;
+  return off;
+}
+
+int32_t check_k(const int32_t* k, int32_t n_levels, int T) {
+  if (n_levels < 0 || n_levels > RECSA_MAX_LEVELS)
+    return fail(RECSA_ERR_INVALID_ARG, "n_levels must be in 0..%d", RECSA_MAX_LEVELS);
+  if (n_levels < T) return fail(RECSA_ERR_INVALID_ARG, "n_levels (%d) is below the tree height (%d)", n_levels, T);
+  if (n_levels > 0 && !k) return fail(RECSA_ERR_INVALID_ARG, "k_per_level is NULL");
+  for (int i = 0; i < n_levels; ++i)
+    if (k[i] < 0) return fail(RECSA_ERR_INVALID_ARG, "k_per_level[%d] = %d is negative", i, k[i]);
+  return RECSA_OK;
+}
+
+// Data-independent bounds over every visible prefix n <= n_max:
+// B_l >= C_l(n), S_l = min(k_l, B_l) >= s_l(n); C_0 <= c0.
+struct Bounds {
+  int64_t smax = 1, csel = 1, c0 = 0, P = 0;
+  int T = 0;
+};
+
+Bounds bounds_for(const Info& I, int64_t n_max, const int32_t* k) {
+  Bounds bd;
+  const int T = levels_of(n_max, I.f);
+  bd.T = T;
+  int64_t S_up = 0, Pmax = 0;
+  for (int lv = T; lv >= 1; --lv) {
+    const int64_t Bl = std::min(nodes_at(n_max, I.f, lv), I.f * S_up + I.f - 1);
+    const int64_t Sl = std::min<int64_t>(k[lv - 1], Bl);
+    bd.smax = std::max(bd.smax, Sl);
+    if (k[lv - 1] < Bl) bd.csel = std::max(bd.csel, Bl);
+    Pmax = std::max(Pmax, Bl);
+    S_up = Sl;
+  }
+  bd.c0 = T ? std::min(n_max, I.f * S_up + I.f - 1) : n_max;
+  bd.P = std::max(Pmax, bd.c0);
+  return bd;
+}
+
+int32_t max_kept(int64_t n, int64_t f, const int32_t* k) {
+  const int T = levels_of(n, f);
+  int64_t s_up = 0, best = 0;
+  for (int lv = T; lv >= 1; --lv) {
+    const int64_t C = f * s_up + (nodes_at(n, f, lv) - f * nodes_at(n, f, lv + 1));
+    const int64_t s = std::min<int64_t>(k[lv - 1], C);
+    best = std::max(best, s);
+    s_up = s;
+  }
+  return static_cast<int32_t>(best);
+}
+
+int64_t table_bytes(const Info& I, int64_t P) {
+  if (I.theta == 0.0f) return 0;
+  return ((P + 1) * (I.d / 2) * static_cast<int64_t>(sizeof(float2)) + kTableAlign - 1) / kTableAlign * kTableAlign;
+}
+
+int32_t fill_table(const Info& I, int64_t P, void* ws, hipStream_t st) {
+  if (I.theta == 0.0f) return RECSA_OK;
+  recsa::InvFreq iv{};
+  for (int i = 0; i < I.d / 2; ++i)
+    iv.w[i] = static_cast<float>(std::pow(static_cast<double>(I.theta), -2.0 * i / static_cast<double>(I.d)));
+  hipError_t e = recsa::launch_rope_table(static_cast<float2*>(ws), P, static_cast<int>(I.d / 2), iv, st);
+  if (e != hipSuccess) return hip_fail(e, "RoPE table launch");
+  return RECSA_OK;
+}
+
+int32_t run_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, const void* K, const void* V,
+                   const void* tree, int64_t n_fixed, int64_t q_start, bool prefill, const int32_t* k,
+                   int32_t n_levels, float* out, float* lse, int32_t* sel, int32_t sel_width, void* ws,
+                   int64_t ws_bytes, void* stream) {
+  Info I;
+  int32_t rc = check_shape(shape, &I);
+  if (rc) return rc;
+  if (n_q < 0) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 0");
+  if (n_q * I.Hkv > INT32_MAX || I.B > 65535) return fail(RECSA_ERR_UNSUPPORTED, "grid too large");
+  const int64_t n_max = prefill ? q_start + n_q : n_fixed;
+  const int64_t n_min = prefill ? q_start + 1 : n_fixed;
+  if (prefill && q_start < 0) return fail(RECSA_ERR_INVALID_ARG, "q_start must be >= 0");
+  if (!prefill && n_fixed < 0) return fail(RECSA_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (n_max > I.cap) return fail(RECSA_ERR_CAPACITY, "%lld tokens exceed the capacity %lld", (long long)n_max,
+                                 (long long)I.cap);
+  rc = check_k(k, n_levels, levels_of(n_max, I.f));
+  if (rc) return rc;
+  if (n_q == 0) return RECSA_OK;
+  if (!q || !out || (n_max > 0 && (!K || !V)) || (levels_of(n_max, I.f) > 0 && !tree))
+    return fail(RECSA_ERR_INVALID_ARG, "q, K, V, tree or out is NULL");
+  if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(tree) || !aligned16(out) || !aligned16(ws))
+    return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (sel) {
+    int32_t need = 0;
+    for (int64_t n = n_min; n <= n_max; ++n) need = std::max(need, max_kept(n, I.f, k));
+    if (sel_width < need) return fail(RECSA_ERR_INVALID_ARG, "sel_width %d < %d kept nodes", sel_width, need);
+  }
+  const Bounds bd = bounds_for(I, n_max, k);
+  if (bd.smax > kMaxList || bd.csel > kMaxList)
+    return fail(RECSA_ERR_UNSUPPORTED, "candidate lists up to %lld entries exceed %lld", (long long)std::max(bd.smax, bd.csel),
+                (long long)kMaxList);
+  const int ch0 = static_cast<int>(std::max<int64_t>(256, std::min<int64_t>(bd.csel, 512)));
+  const size_t lds = recsa::attend_lds_bytes(static_cast<int>(I.d), static_cast<int>(I.G), static_cast<int>(bd.smax),
+                                             static_cast<int>(bd.csel), ch0);
+  if (lds > kMaxLds) return fail(RECSA_ERR_UNSUPPORTED, "needs %zu bytes of LDS (max %zu)", lds, kMaxLds);
+  const int64_t need_ws = table_bytes(I, bd.P);
+  if (ws_bytes < need_ws) return fail(RECSA_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes, (long long)need_ws);
+  if (need_ws > 0 && !ws) return fail(RECSA_ERR_INVALID_ARG, "workspace is NULL");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = fill_table(I, bd.P, ws, st);
+  if (rc) return rc;
+
+  recsa::AttnArgs a{};
+  a.q = q;
+  a.K = K;
+  a.V = V;
+  a.out = out;
+  a.lse = lse;
+  a.sel = sel;
+  a.tab = static_cast<const float2*>(ws);
+  a.cap = I.cap;
+  a.n_q = n_q;
+  a.n_fixed = n_fixed;
+  a.q_start = q_start;
+  a.prefill = prefill ? 1 : 0;
+  a.Hkv = static_cast<int32_t>(I.Hkv);
+  a.Hq = static_cast<int32_t>(I.Hq);
+  a.f = static_cast<int32_t>(I.f);
+  a.n_levels = n_levels;
+  a.sel_width = sel_width;
+  a.scale = I.scale;
+  a.use_rope = I.theta != 0.0f;
+  a.smax = static_cast<int32_t>(bd.smax);
+  a.csel = static_cast<int32_t>(bd.csel);
+  a.ch0 = ch0;
+  for (int lv = 1; lv <= RECSA_MAX_LEVELS; ++lv) a.k.k[lv] = lv <= n_levels ? k[lv - 1] : 0;
+  const int Tc = levels_of(I.cap, I.f);
+  for (int lv = 1; lv <= Tc && lv <= RECSA_MAX_LEVELS; ++lv) {
+    a.tree.NK[lv] = static_cast<const char*>(tree) + level_offset_bytes(I, lv, 0);
+    a.tree.NV[lv] = static_cast<const char*>(tree) + level_offset_bytes(I, lv, 1);
+    a.tree.rows[lv] = nodes_at(I.cap, I.f, lv);
+  }
+  hipError_t e = recsa::launch_attend(a, static_cast<int>(I.d), I.bf16, static_cast<int>(I.G), lds, I.B, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return RECSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t recsa_abi_version(void) { return RECSA_ABI_VERSION; }
+
+const char* recsa_last_error(void) { return g_err.c_str(); }
+
+int32_t recsa_num_levels(int64_t n_tokens, int32_t fanout) {
+  if (n_tokens < 0 || fanout < 2) return -1;
+  return levels_of(n_tokens, fanout);
+}
+
+int64_t recsa_tree_bytes(const recsa_shape_t* shape) {
+  Info I;
+  if (check_shape(shape, &I)) return -1;
+  return level_offset_bytes(I, levels_of(I.cap, I.f) + 1, 0);
+}
+
+int64_t recsa_level_offset(const recsa_shape_t* shape, int32_t level, int32_t which) {
+  Info I;
+  if (check_shape(shape, &I)) return -1;
+  if (level < 1 || level > levels_of(I.cap, I.f) || (which != 0 && which != 1)) {
+    fail(RECSA_ERR_INVALID_ARG, "level %d / which %d out of range", level, which);
+    return -1;
+  }
+  return level_offset_bytes(I, level, which);
+}
+
+int32_t recsa_sel_width(const recsa_shape_t* shape, int64_t n_min, int64_t n_max, const int32_t* k, int32_t n_levels) {
+  Info I;
+  if (check_shape(shape, &I)) return -1;
+  if (n_min < 0 || n_max < n_min) {
+    fail(RECSA_ERR_INVALID_ARG, "need 0 <= n_min <= n_max");
+    return -1;
+  }
+  if (check_k(k, n_levels, levels_of(n_max, I.f))) return -1;
+  int32_t need = 0;
+  for (int64_t n = n_min; n <= n_max; ++n) need = std::max(need, max_kept(n, I.f, k));
+  return need;
+}
+
+int64_t recsa_workspace_bytes(const recsa_shape_t* shape, int64_t n_max, const int32_t* k, int32_t n_levels) {
+  Info I;
+  if (check_shape(shape, &I)) return -1;
+  if (n_max < 0) {
+    fail(RECSA_ERR_INVALID_ARG, "n_max must be >= 0");
+    return -1;
+  }
+  if (!k) return table_bytes(I, n_max);  // dense: positions 0..n_max
+  if (check_k(k, n_levels, levels_of(n_max, I.f))) return -1;
+  return table_bytes(I, bounds_for(I, n_max, k).P);
+}
+
+int32_t recsa_build_tree(const recsa_shape_t* shape, const void* K, const void* V, const void* W, int64_t n_old,
+                         int64_t n_new, void* tree, void* stream) {
+  Info I;
+  int32_t rc = check_shape(shape, &I);
+  if (rc) return rc;
+  if (n_old < 0 || n_new < n_old) return fail(RECSA_ERR_INVALID_ARG, "need 0 <= n_old <= n_new");
+  if (n_new > I.cap) return fail(RECSA_ERR_CAPACITY, "n_new %lld exceeds the capacity %lld", (long long)n_new, (long long)I.cap);
+  const int T = levels_of(n_new, I.f);
+  if (nodes_at(n_old, I.f, 1) == nodes_at(n_new, I.f, 1)) return RECSA_OK;  // no node completes
+  if (!K || !V || !W || !tree) return fail(RECSA_ERR_INVALID_ARG, "K, V, W or tree is NULL");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(tree))
+    return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int lv = 1; lv <= T; ++lv) {
+    const int64_t lo = nodes_at(n_old, I.f, lv), hi = nodes_at(n_new, I.f, lv);
+    if (hi <= lo) continue;
+    recsa::PoolArgs p{};
+    if (lv == 1) {
+      p.srcK = K;
+      p.srcV = V;
+      p.src_rows = I.cap;
+    } else {
+      p.srcK = static_cast<const char*>(tree) + level_offset_bytes(I, lv - 1, 0);
+      p.srcV = static_cast<const char*>(tree) + level_offset_bytes(I, lv - 1, 1);
+      p.src_rows = nodes_at(I.cap, I.f, lv - 1);
+    }
+    p.dstK = static_cast<char*>(tree) + level_offset_bytes(I, lv, 0);
+    p.dstV = static_cast<char*>(tree) + level_offset_bytes(I, lv, 1);
+    p.dst_rows = nodes_at(I.cap, I.f, lv);
+    p.W = W;
+    p.g_lo = lo;
+    p.g_hi = hi;
+    p.f = static_cast<int32_t>(I.f);
+    p.BH = static_cast<int32_t>(I.B * I.Hkv);
+    hipError_t e = recsa::launch_pool_level(p, static_cast<int>(I.d), I.bf16, st);
+    if (e != hipSuccess) return hip_fail(e, "tree build launch");
+  }
+  return RECSA_OK;
+}
+
+int32_t recsa_decode(const recsa_shape_t* shape, const void* q, int64_t n_q, const void* K, const void* V,
+                     const void* tree, int64_t n_tokens, const int32_t* k, int32_t n_levels, float* out, float* lse,
+                     int32_t* sel, int32_t sel_width, void* workspace, int64_t ws_bytes, void* stream) {
+  return run_attend(shape, q, n_q, K, V, tree, n_tokens, 0, false, k, n_levels, out, lse, sel, sel_width, workspace,
+                    ws_bytes, stream);
+}
+
+int32_t recsa_prefill(const recsa_shape_t* shape, const void* q, int64_t q_start, int64_t n_q, const void* K,
+                      const void* V, const void* tree, const int32_t* k, int32_t n_levels, float* out, float* lse,
+                      int32_t* sel, int32_t sel_width, void* workspace, int64_t ws_bytes, void* stream) {
+  return run_attend(shape, q, n_q, K, V, tree, 0, q_start, true, k, n_levels, out, lse, sel, sel_width, workspace,
+                    ws_bytes, stream);
+}
+
+int32_t recsa_dense_ref_attn(const recsa_shape_t* shape, const void* q, int64_t q_start, int64_t n_q, const void* K,
+                             const void* V, int64_t n_tokens, int32_t causal, float* out, float* lse, void* workspace,
+                             int64_t ws_bytes, void* stream) {
+  (void)q; (void)q_start; (void)n_q; (void)K; (void)V; (void)n_tokens; (void)causal; (void)out; (void)lse;
+  (void)workspace; (void)ws_bytes; (void)stream;
+  Info I;
+  int32_t rc = check_shape(shape, &I);
+  if (rc) return rc;
+  return fail(RECSA_ERR_UNSUPPORTED, "dense reference attention is not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Host <-> kernel interface of the RecSA library (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "recsa.h"
+
+namespace recsa {
+
+// ---------------------------------------------------------------- tree build
+// One launch pools the nodes [g_lo, g_hi) of one level for every (sequence, KV head).
+struct PoolArgs {
+  const void* srcK;     // children: token rows (level 1) or level-(l-1) node keys
+  const void* srcV;
+  int64_t src_rows;     // child rows per (sequence, KV head) slice
+  void* dstK;           // level-l node keys / values
+  void* dstV;
+  int64_t dst_rows;     // node rows per slice
+  const void* W;        // [d][d] pooler
+  int64_t g_lo, g_hi;   // node range to build
+  int32_t f;
+  int32_t BH;           // batch * n_kv_heads
+};
+hipError_t launch_pool_level(const PoolArgs& a, int d, bool bf16, hipStream_t s);
+
+// ---------------------------------------------------------------- RoPE table
+struct InvFreq {
+  float w[64];  // omega_i, i < d/2
+};
+// tab[p * (d/2) + i] = (cos(p * omega_i), sin(p * omega_i)), evaluated in float64, for p = 0..P.
+hipError_t launch_rope_table(float2* tab, int64_t P, int half, const InvFreq& iv, hipStream_t s);
+
+// ---------------------------------------------------------------- descent + softmax
+struct TreeLevels {
+  const void* NK[RECSA_MAX_LEVELS + 1];  // index = level (1-based); [B*H_kv][rows[l]][d]
+  const void* NV[RECSA_MAX_LEVELS + 1];
+  int64_t rows[RECSA_MAX_LEVELS + 1];
+};
+
+struct LevelK {
+  int32_t k[RECSA_MAX_LEVELS + 1];  // index = level (1-based)
+};
+
+struct AttnArgs {
+  const void* q;        // [B][n_q][H_q][d]
+  const void* K;        // [B*H_kv][cap][d]
+  const void* V;
+  float* out;           // [B][n_q][H_q][d]
+  float* lse;           // [B][n_q][H_q] or null
+  int32_t* sel;         // [B][n_q][H_kv][n_levels][sel_width] or null
+  const float2* tab;    // RoPE table, rows 0..P
+  int64_t cap;
+  int64_t n_q;
+  int64_t n_fixed;      // decode: visible tokens
+  int64_t q_start;      // prefill: position of query 0
+  int32_t prefill;      // 1: query j sees n = q_start + j + 1 tokens, own token included
+  int32_t Hkv, Hq, f;
+  int32_t n_levels, sel_width;
+  float scale;
+  int32_t use_rope;
+  int32_t smax;         // capacity of a kept-node list
+  int32_t csel;         // capacity of a scored candidate list at a selecting level
+  int32_t ch0;          // token-level chunk
+  LevelK k;
+  TreeLevels tree;
+};
+
+size_t attend_lds_bytes(int d, int G, int smax, int csel, int ch0);
+hipError_t launch_attend(const AttnArgs& a, int d, bool bf16, int G, size_t lds, int64_t B, hipStream_t s);
+
+}  // namespace recsa

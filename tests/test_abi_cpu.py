@@ -1,0 +1,126 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry point, sizes
+buffers as documented, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_hierarchical_amd import recsa as R
+from oracle import level_counts, plan_counts
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "recsa.h")).read()
+    return sorted(set(re.findall(r"\b(recsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = R.lib()
+    names = _declared()
+    assert set(names) == set(R.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert R.recsa_abi_version() == 1
+
+
+def _shape(**kw):
+    base = dict(batch=2, n_kv_heads=8, n_q_heads=32, head_dim=128, fanout=16, dtype="bf16",
+                capacity=1 << 20, rope_theta=1.0e6)
+    base.update(kw)
+    return R.Shape(**base)
+
+
+def test_levels_and_tree_layout():
+    for n, f in [(0, 16), (15, 16), (16, 16), (4096, 16), (4095, 16), (131072, 16), (2 ** 21, 32), (1000, 3)]:
+        assert R.recsa_num_levels(n, f) == len(level_counts(n, f))
+    sh = _shape()
+    T = R.recsa_num_levels(sh.capacity, sh.fanout)
+    total, off = 0, 0
+    for lv in range(1, T + 1):
+        rows = sh.capacity // sh.fanout ** lv
+        blk = sh.batch * sh.n_kv_heads * rows * sh.head_dim * 2
+        assert R.recsa_level_offset(sh, lv, 0) == off
+        assert R.recsa_level_offset(sh, lv, 1) == off + blk
+        off += 2 * blk
+    assert R.recsa_tree_bytes(sh) == off
+
+
+@pytest.mark.parametrize("n,f,k", [(4096, 16, 4), (131072, 16, 8), (2 ** 21, 32, 16), (5000, 16, 8), (777, 4, 3)])
+def test_sel_width_matches_closed_form(n, f, k):
+    sh = _shape(fanout=f, capacity=max(n, 1))
+    T = R.recsa_num_levels(n, f)
+    ks = [k] * T
+    C, s, _ = plan_counts(n, f, ks)
+    assert R.recsa_sel_width(sh, n, n, ks) == max(s.values(), default=0)
+    lo = max(1, n - 300)
+    want = 0
+    for m in range(lo, n + 1):
+        _, sm, _ = plan_counts(m, f, ks + [k] * 4)
+        want = max(want, max(sm.values(), default=0))
+    assert R.recsa_sel_width(sh, lo, n, ks) == want
+
+
+def test_workspace_holds_the_rope_table():
+    sh = _shape(head_dim=128)
+    k = [8] * 4
+    nb = R.recsa_workspace_bytes(sh, 131072, k)
+    # positions 0..max candidates (f*k + f - 1 = 143) of (cos, sin) float32 pairs, 256-byte aligned
+    assert nb == ((143 + 1) * 64 * 8 + 255) // 256 * 256
+    assert R.recsa_workspace_bytes(_shape(rope_theta=0.0), 131072, k) == 0
+
+
+def _status(fn, *args):
+    with pytest.raises(R.RecsaError) as e:
+        fn(*args)
+    return e.value.code
+
+
+class _FakeTensor:
+    """A pointer-only stand-in: validation must reject the call before touching it."""
+
+    def __init__(self, addr=0x1000, shape=(1, 1, 1, 1)):
+        self._addr, self.shape = addr, shape
+
+    def data_ptr(self):
+        return self._addr
+
+    def numel(self):
+        return 1 << 30
+
+    def element_size(self):
+        return 1
+
+
+class _NoStream:
+    cuda_stream = 0
+
+
+def test_error_paths_return_status_before_launch():
+    t = _FakeTensor()
+    ns = _NoStream()
+    sh = _shape(capacity=4096)
+    k = [8] * 3
+    bad_heads = _shape(n_q_heads=30)
+    assert _status(R.recsa_build_tree, bad_heads, t, t, t, 0, 16, t, ns) == -1
+    assert _status(R.recsa_build_tree, _shape(head_dim=96), t, t, t, 0, 16, t, ns) == -3
+    assert _status(R.recsa_build_tree, _shape(fanout=1), t, t, t, 0, 16, t, ns) == -3
+    assert _status(R.recsa_build_tree, sh, t, t, t, 0, 5000, t, ns) == -2
+    assert _status(R.recsa_build_tree, sh, t, t, t, 20, 10, t, ns) == -1
+    assert _status(R.recsa_build_tree, sh, None, t, t, 0, 4096, t, ns) == -1
+    assert _status(R.recsa_build_tree, sh, _FakeTensor(0x1008), t, t, 0, 4096, t, ns) == -1
+    q = _FakeTensor(shape=(2, 4, 32, 128))
+    assert _status(R.recsa_decode, sh, q, t, t, t, 5000, k, t, None, None, 0, t, ns) == -2
+    assert _status(R.recsa_decode, sh, q, t, t, t, 4096, [8, 8], t, None, None, 0, t, ns) == -1
+    assert _status(R.recsa_decode, sh, q, t, t, t, 4096, [8, -1, 8], t, None, None, 0, t, ns) == -1
+    assert _status(R.recsa_decode, sh, q, t, t, t, 4096, k, t, None, t, 1, t, ns) == -1  # sel_width too small
+    small_ws = _FakeTensor()
+    small_ws.numel = lambda: 16
+    assert _status(R.recsa_decode, sh, q, t, t, t, 4096, k, t, None, None, 0, small_ws, ns) == -5
+    assert _status(R.recsa_prefill, sh, q, 4094, t, t, t, k, t, None, None, 0, t, ns) == -2
+    assert _status(R.recsa_prefill, sh, q, -1, t, t, t, k, t, None, None, 0, t, ns) == -1
+    assert _status(R.recsa_decode, _shape(capacity=1 << 20), q, t, t, t, 1 << 20, [1 << 30] * 5, t, None, None, 0,
+                   t, ns) == -3                                                          # lists beyond LDS
+    assert "capacity" in R.lib().recsa_last_error().decode() or R.lib().recsa_last_error()

@@ -1,0 +1,207 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on seeded inputs.
+
+Selections must be identical level by level (a flagged near tie, relative score gap below
+1e-5, may split either way); outputs within 2e-3 (bf16 storage) or 1e-5 (float32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, Gpu, compare_unit, storage_bits
+from synthetic import WORKLOADS, Workload, gen_decode_inputs, with_overrides
+
+pytestmark = pytest.mark.gpu
+INT32_MAX = oracle.INT32_MAX
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _check_units(w, inp, res, k, units, mode, n_tokens=None, q_start=0, min_match=0.9):
+    out, lse, sel, _ = res
+    if mode == "decode":
+        ref = oracle.decode(inp["K"], inp["V"], inp["W"], inp["q"], n_tokens, w.f, k, w.dtype, w.theta, units=units)
+    else:
+        qs = inp["q"][:, q_start:q_start + out.shape[1]]
+        ref = oracle.prefill(inp["K"], inp["V"], inp["W"], qs, q_start, w.f, k, w.dtype, w.theta, units=units)
+    G = w.G
+    stats = {"match": 0, "excused": 0}
+    for (b, j, h), r in ref.items():
+        st = compare_unit(r, sel[b, j, h], out[b, j, h * G:(h + 1) * G], lse[b, j, h * G:(h + 1) * G],
+                          TOL[w.dtype], where=f"{w.name} unit {(b, j, h)}")
+        stats[st] += 1
+    assert stats["match"] >= min_match * len(ref), stats
+    return stats
+
+
+def _w(name="t", B=1, Hq=4, Hkv=1, d=64, dtype="f32", L=4096, f=16, k=4, n_queries=4, **kw):
+    std = kw.pop("std", 1.0 if dtype == "f32" else d ** -0.5)
+    return Workload(name, B=B, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, L=L, f=f, k=k, n_queries=n_queries,
+                    mode="decode", std=std, **kw)
+
+
+# ------------------------------------------------------------------ tree build
+
+BUILD_CASES = [
+    _w("b_f32_d64_f16", L=4096 + 77, seed=1),
+    _w("b_bf16_d128_f16", Hq=8, Hkv=2, d=128, dtype="bf16", L=16 ** 3 * 3 + 250, seed=2),
+    _w("b_bf16_d128_f32", Hq=4, Hkv=1, d=128, dtype="bf16", L=32 ** 2 * 5 + 31, f=32, seed=3),
+    _w("b_f32_d64_f3", L=3 ** 7 + 5, f=3, seed=4),
+    _w("b_bf16_d64_f5", B=2, Hq=2, Hkv=2, d=64, dtype="bf16", L=5 ** 5 + 9, f=5, seed=5),
+]
+
+
+@pytest.mark.parametrize("w", BUILD_CASES, ids=lambda w: w.name)
+def test_tree_build_bitwise(w):
+    """Every node key and value equals the oracle's bit for bit, built in several increments."""
+    _say(f"build {w.name}")
+    inp = gen_decode_inputs(w, n_q=1)
+    g = Gpu(w, inp, build=False)
+    cuts = [0, 1, w.f - 1, w.f ** 2 + 3, w.L // 2, w.L - 1, w.L]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        from long_context_hierarchical_amd import recsa as R
+        R.recsa_build_tree(g.shape, g.K, g.V, g.W, a, b, g.tree)
+    torch.cuda.synchronize()
+    from long_context_hierarchical_amd import recsa as R
+    Wf = oracle.from_storage(inp["W"], w.dtype)
+    T = oracle.level_counts(w.L, w.f)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            Kf = oracle.from_storage(inp["K"][b, h], w.dtype)
+            Vf = oracle.from_storage(inp["V"][b, h], w.dtype)
+            tree = oracle.build_slice(Kf, Vf, Wf, w.f, w.dtype, n_new=w.L)
+            for lv in range(1, len(T) + 1):
+                NK, NV = R.tree_level_views(g.shape, g.tree, lv)
+                want_k = oracle.to_storage(tree[lv - 1][0], w.dtype)
+                want_v = oracle.to_storage(tree[lv - 1][1], w.dtype)
+                got_k = storage_bits(NK[b, h])
+                got_v = storage_bits(NV[b, h])
+                wk = want_k.view(got_k.dtype)
+                wv = want_v.view(got_v.dtype)
+                assert np.array_equal(got_v, wv), f"values differ at level {lv}: {np.sum(got_v != wv)} elements"
+                assert np.array_equal(got_k, wk), f"keys differ at level {lv}: {np.sum(got_k != wk)} elements"
+
+
+def test_rope_table_bitwise():
+    """The (cos, sin) table the kernels read equals the oracle's bit for bit."""
+    w = _w("tab", Hq=32, Hkv=8, d=128, dtype="bf16", L=16 ** 4 + 100, f=16, k=8, n_queries=1, seed=6)
+    inp = gen_decode_inputs(w, n_q=1, heads=[0])
+    g = Gpu(w, inp)
+    k = [8] * 4
+    _, _, _, ws = g.decode(k, w.L)
+    P = 16 * 8 + 16 - 1
+    got = ws[:(P + 1) * 64 * 8].view(torch.float32).view(P + 1, 64, 2).cpu().numpy()
+    c, s = oracle.rope_table(P, 128, w.theta)
+    assert np.array_equal(got[..., 0].view(np.uint32), c.view(np.uint32))
+    assert np.array_equal(got[..., 1].view(np.uint32), s.view(np.uint32))
+
+
+# ------------------------------------------------------------------ decode
+
+def test_decode_tiny_workload_full():
+    """The 4K-token float32 workload: every query, every unit."""
+    w = WORKLOADS["c0"]
+    _say("decode c0")
+    inp = gen_decode_inputs(w)
+    g = Gpu(w, inp)
+    k = [w.k] * 3
+    res = g.decode(k, w.L)
+    units = [(0, j, 0) for j in range(w.n_queries)]
+    _check_units(w, inp, res, k, units, "decode", n_tokens=w.L, min_match=1.0)
+
+
+DECODE_CASES = [
+    # (workload, k per level, n_tokens offset from L)
+    (_w("d_bf16_G4_f16_ragged", Hq=8, Hkv=2, d=128, dtype="bf16", L=5000, k=8, n_queries=3, seed=11), [8] * 3),
+    (_w("d_bf16_G8_f32", Hq=16, Hkv=2, d=128, dtype="bf16", L=40000, f=32, k=16, n_queries=2, seed=12), [16] * 3),
+    (_w("d_f32_G1_f3", Hq=2, Hkv=2, d=64, dtype="f32", L=1000, f=3, k=2, n_queries=3, seed=13), [2, 3, 1, 2, 2, 4]),
+    (_w("d_bf16_G2_f4_mixedk", B=2, Hq=4, Hkv=2, d=64, dtype="bf16", L=777, f=4, n_queries=2, seed=14),
+     [0, 3, 1, 5]),
+    (_w("d_f32_norope", d=64, L=3000, k=4, n_queries=3, theta=0.0, seed=15), [4, 4]),
+    (_w("d_f32_T0", d=64, L=13, k=4, n_queries=2, seed=16), [4]),
+    (_w("d_bf16_nopruning", Hq=8, Hkv=2, d=128, dtype="bf16", L=3000, k=4, n_queries=2, seed=17), [INT32_MAX] * 2),
+    (_w("d_f32_k0", d=64, L=4096 + 300, k=0, n_queries=2, seed=18), [0, 0, 0]),
+    (_w("d_bf16_G4_f16_big_k", Hq=4, Hkv=1, d=128, dtype="bf16", L=16 ** 3 * 4, k=20, n_queries=2, seed=19),
+     [20, 20, 20]),
+]
+
+
+@pytest.mark.parametrize("w,k", DECODE_CASES, ids=lambda x: getattr(x, "name", ""))
+def test_decode_variants(w, k):
+    _say(f"decode {w.name}")
+    inp = gen_decode_inputs(w)
+    g = Gpu(w, inp)
+    res = g.decode(k, w.L)
+    units = [(b, j, h) for b in range(w.B) for j in range(w.n_queries) for h in range(w.Hkv)]
+    _check_units(w, inp, res, k, units, "decode", n_tokens=w.L)
+
+
+def test_decode_on_a_shorter_prefix_and_empty_cache():
+    """The tree holds more nodes than the visible prefix; nodes beyond it must be ignored.
+    With no visible token, out = 0 and lse = -inf."""
+    w = _w("prefix", Hq=8, Hkv=2, d=128, dtype="bf16", L=9000, k=8, n_queries=2, seed=21)
+    inp = gen_decode_inputs(w)
+    g = Gpu(w, inp)
+    for n in (8191, 4096, 300, 16, 15, 1):
+        k = [8] * max(1, oracle.level_counts(n, 16).__len__())
+        res = g.decode(k, n)
+        units = [(0, j, h) for j in range(2) for h in range(2)]
+        _check_units(w, inp, res, k, units, "decode", n_tokens=n)
+    out, lse, sel, _ = g.decode([8], 0)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_decode_is_deterministic():
+    w = _w("det", Hq=32, Hkv=8, d=128, dtype="bf16", L=70000, k=8, n_queries=8, seed=22)
+    inp = gen_decode_inputs(w)
+    g = Gpu(w, inp)
+    k = [8] * 4
+    a = g.decode(k, w.L)
+    b = g.decode(k, w.L)
+    assert np.array_equal(a[2], b[2])
+    assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
+
+
+# ------------------------------------------------------------------ prefill
+
+def test_prefill_matches_oracle_and_chunking():
+    """Causal prefill: sampled positions (edges of blocks and levels included) against the
+    oracle, and the same positions computed in uneven chunks give bitwise-identical results."""
+    w = _w("pf", Hq=8, Hkv=2, d=128, dtype="bf16", L=5000, k=8, n_queries=5000, seed=31)
+    _say("prefill")
+    inp = gen_decode_inputs(w)
+    g = Gpu(w, inp)
+    k = [8] * 3
+    full = g.prefill(k, 0, w.L)
+    rng = np.random.default_rng(0)
+    pos = sorted(set([0, 1, 14, 15, 16, 17, 255, 256, 257, 4095, 4096, 4097, w.L - 1] +
+                     rng.integers(0, w.L, 40).tolist()))
+    units = [(0, int(p), h) for p in pos for h in range(w.Hkv)]
+    _check_units(w, inp, full, k, units, "prefill", q_start=0)
+    cuts = [0, 1000, 1001, 3333, w.L]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        part = g.prefill(k, a, b - a)
+        assert np.array_equal(part[2], full[2][:, a:b]), (a, b)
+        assert np.array_equal(part[0].view(np.uint32), full[0][:, a:b].view(np.uint32)), (a, b)
+
+
+def test_prefill_with_incremental_tree():
+    """Chunked prefill where the tree is extended chunk by chunk, as a serving loop does."""
+    w = _w("pf_inc", Hq=8, Hkv=2, d=64, dtype="f32", L=3000, f=4, k=3, n_queries=3000, seed=32)
+    inp = gen_decode_inputs(w)
+    g = Gpu(w, inp, build=False)
+    from long_context_hierarchical_amd import recsa as R
+    k = [3] * 6
+    outs = []
+    for a in range(0, w.L, 700):
+        b = min(w.L, a + 700)
+        R.recsa_build_tree(g.shape, g.K, g.V, g.W, a, b, g.tree)
+        outs.append(g.prefill(k, a, b - a))
+    sel = np.concatenate([o[2] for o in outs], axis=1)
+    out = np.concatenate([o[0] for o in outs], axis=1)
+    lse = np.concatenate([o[1] for o in outs], axis=1)
+    pos = [0, 3, 4, 15, 16, 63, 64, 699, 700, 701, 2047, 2048, 2999] + list(range(1200, 1230))
+    units = [(0, p, h) for p in pos for h in range(2)]
+    _check_units(w, inp, (out, lse, sel, None), k, units, "prefill", q_start=0)
