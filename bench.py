@@ -1,0 +1,286 @@
+"""Benchmark: RecSA tree attention on one MI355X.
+
+Workload (default): four independent sequences of 524,288 cached tokens, 32 query heads over
+8 KV heads, head_dim 128, bf16, fanout 16, k = 8 per level, keys from a 64-centre Gaussian
+mixture with planted needles; 256 decode queries per sequence.
+
+One step = the whole hot path on that batch: build the tree over all 4 x 524,288 tokens
+(node keys and mean values for every level), then decode all 4 x 256 queries (descent,
+level-index RoPE, per-level top-k, one softmax) in one call. Inputs are resident in HBM
+before timing starts. `value` is decode queries per second of whole-step time.
+
+Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+METRIC = "decode queries/s & prefill tok/s per layer at 524K; % of HBM/MFMA roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-units", type=int, default=24, help="oracle decode units timed for the baseline")
+    ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--step-mode", action="store_true", help="also time one-query-per-sequence decode calls")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_hierarchical_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, src_hash: str):
+    """HBM bytes per launch measured with rocprofv3 counters for this exact kernel source, if recorded."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def decode_bytes_per_query(w, k):
+    """Rows one query must read (all KV heads): node keys of every scored level, node values of
+    every unkept candidate, and the key and value of every token-level candidate."""
+    from long_context_hierarchical_amd.recsa import recsa_num_levels  # noqa: F401  (library sizing check)
+    T = 0
+    m = w.L // w.f
+    nl = []
+    while m >= 1:
+        nl.append(m)
+        m //= w.f
+        T += 1
+    s_up, n_up, key_rows, val_rows = 0, 0, 0, 0
+    for lv in range(T, 0, -1):
+        C = w.f * s_up + (nl[lv - 1] - w.f * n_up)
+        s = min(k[lv - 1], C)
+        if s < C:
+            key_rows += C
+            val_rows += C - s
+        s_up, n_up = s, nl[lv - 1]
+    C0 = w.f * s_up + (w.L - w.f * n_up) if T else w.L
+    rows = key_rows + val_rows + 2 * C0
+    return rows * w.d * w.elem_bytes * w.Hkv, dict(key_rows=key_rows, val_rows=val_rows, tok_rows=C0)
+
+
+def build_bytes(w):
+    """Read every token row of K and V once, write every node key and value once (all levels)."""
+    nodes, m = 0, w.L // w.f
+    while m >= 1:
+        nodes += m
+        m //= w.f
+    return w.B * w.Hkv * w.d * w.elem_bytes * (2 * w.L + 2 * nodes), nodes
+
+
+def cpu_baseline(w, k, n_units):
+    """The oracle as it stands, single-threaded: build one (sequence, KV head) slice of the tree and
+    decode `n_units` (query, KV head) units, extrapolated to the whole step."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from synthetic import gen_kv_slice, gen_queries, gen_W
+
+    with threadpool_limits(limits=1):
+        q = gen_queries(w, 0)
+        K, V = gen_kv_slice(w, 0, 0, q)
+        W = gen_W(w)
+        Kf, Vf, Wf = (oracle.from_storage(x, w.dtype) for x in (K, V, W))
+        t0 = time.perf_counter()
+        tree = oracle.build_slice(Kf, Vf, Wf, w.f, w.dtype, n_new=w.L)
+        t_build = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for j in range(n_units):
+            qg = oracle.from_storage(q[j, 0:w.G], w.dtype)
+            oracle.attend_unit(qg, Kf, Vf, tree, w.L, w.f, k, w.dtype, w.theta)
+        t_unit = (time.perf_counter() - t0) / n_units
+    step_s = w.B * w.Hkv * t_build + w.B * w.n_queries * w.Hkv * t_unit
+    return {
+        "value": w.B * w.n_queries / step_s,
+        "unit": "queries/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"tree build of 1 of {w.B * w.Hkv} (sequence, KV head) slices ({t_build:.2f} s) and "
+                   f"{n_units} of {w.B * w.n_queries * w.Hkv} decode units ({t_unit * 1e3:.1f} ms each), "
+                   f"extrapolated to one step ({step_s:.1f} s)"),
+        "build_GBps": build_bytes(w)[0] / (w.B * w.Hkv) / t_build / 1e9,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(the path shards by (sequence, KV head) with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from long_context_hierarchical_amd import recsa as R
+    from synthetic import WORKLOADS, gen_kv_slice, gen_queries, gen_W
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    sh = R.Shape(w.B, w.Hkv, w.Hq, w.d, w.f, w.dtype, w.L, 0.0, w.theta)
+    T = R.recsa_num_levels(w.L, w.f)
+    k = [w.k] * T
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if w.dtype == "bf16" else t).to(dev, non_blocking=False)
+
+    log(f"generating {w.name}: B={w.B} L={w.L} Hkv={w.Hkv} d={w.d} {w.dtype}")
+    t0 = time.time()
+    K = torch.empty(w.B, w.Hkv, w.L, w.d, dtype=td, device=dev)
+    V = torch.empty_like(K)
+    q = torch.empty(w.B, w.n_queries, w.Hq, w.d, dtype=td, device=dev)
+    for b in range(w.B):
+        qb = gen_queries(w, b)
+        q[b] = up(qb)
+        for h in range(w.Hkv):
+            Kb, Vb = gen_kv_slice(w, b, h, qb)
+            K[b, h] = up(Kb)
+            V[b, h] = up(Vb)
+    W = up(gen_W(w))
+    log(f"inputs resident ({time.time() - t0:.1f} s)")
+
+    tree = torch.zeros(R.recsa_tree_bytes(sh), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(R.recsa_workspace_bytes(sh, w.L, k), dtype=torch.uint8, device=dev)
+    width = R.recsa_sel_width(sh, w.L, w.L, k)
+    out = torch.empty(w.B, w.n_queries, w.Hq, w.d, dtype=torch.float32, device=dev)
+    lse = torch.empty(w.B, w.n_queries, w.Hq, dtype=torch.float32, device=dev)
+    sel = torch.empty(w.B, w.n_queries, w.Hkv, T, width, dtype=torch.int32, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        R.recsa_build_tree(sh, K, V, W, 0, w.L, tree)
+        if ev:
+            ev[1].record()
+        R.recsa_decode(sh, q, K, V, tree, w.L, k, out, lse, sel, width, ws)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    build_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = wall * 1e3 / args.steps
+    n_queries = w.B * w.n_queries
+
+    bb, n_nodes = build_bytes(w)
+    qb_bytes, rows = decode_bytes_per_query(w, k)
+    db = qb_bytes * n_queries
+    build_launches = T
+    kinfo = {
+        "pool_level_kernel": dict(bytes=bb / build_launches, ms=build_ms / build_launches,
+                                  src=kernel_hash("build_tree.hip", "common.hpp")),
+        "attend_kernel": dict(bytes=db, ms=decode_ms, src=kernel_hash("attend.hip", "common.hpp")),
+    }
+    dom = "pool_level_kernel" if build_ms >= decode_ms else "attend_kernel"
+
+    def roof(name):
+        ki = kinfo[name]
+        ach = ki["bytes"] / (ki["ms"] * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(name, ki["src"]),
+                "kernel": name}
+
+    res = {
+        "metric": METRIC,
+        "value": round(n_queries / (ms_per_step * 1e-3), 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"recsa-{w.name}: tree build + batched decode, B={w.B}, L={w.L}, "
+                               f"Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, fanout={w.f}, k={w.k}, "
+                               f"{w.n_queries} queries/sequence",
+                   "global_batch": n_queries, "seq_len": w.L, "parallelism": "none (1 GPU)"},
+        "roofline": roof(dom),
+        "breakdown": {
+            "build_ms": round(build_ms, 4), "decode_ms": round(decode_ms, 4),
+            "build_GBps": round(bb / (build_ms * 1e-3) / 1e9, 1),
+            "decode_queries_per_s": round(n_queries / (decode_ms * 1e-3), 1),
+            "decode_bytes_per_query": qb_bytes, "decode_rows_per_unit": rows,
+            "build_bytes": bb, "tree_nodes_per_slice": n_nodes,
+            "roofline_other": roof("attend_kernel" if dom == "pool_level_kernel" else "pool_level_kernel"),
+        },
+    }
+
+    if args.step_mode:
+        one_q = q[:, :1].contiguous()
+        o1 = torch.empty(w.B, 1, w.Hq, w.d, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            R.recsa_decode(sh, one_q, K, V, tree, w.L, k, o1, None, None, 0, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_calls = 64
+        q_steps = [q[:, i:i + 1].contiguous() for i in range(n_calls)]
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n_calls):
+            R.recsa_decode(sh, q_steps[i], K, V, tree, w.L, k, o1, None, None, 0, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        per = e0.elapsed_time(e1) / n_calls
+        res["breakdown"]["step_mode"] = {"ms_per_call": round(per, 4), "queries_per_call": w.B,
+                                         "queries_per_s": round(w.B / (per * 1e-3), 1)}
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        res["breakdown"]["calib_copy_bytes"] = 1 << 30
+
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline(w, k, args.cpu_units)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
