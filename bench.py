@@ -136,7 +136,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(the path shards by (sequence, KV head) with no exchange; see the design notes).",
+              f"(the path shards by (sequence, KV head) with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -191,9 +191,9 @@ int32_t run_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, const
   if (bd.smax > kMaxList || bd.csel > kMaxList)
     return fail(RECSA_ERR_UNSUPPORTED, "candidate lists up to %lld entries exceed %lld", (long long)std::max(bd.smax, bd.csel),
                 (long long)kMaxList);
-  const int ch0 = static_cast<int>(std::max<int64_t>(256, std::min<int64_t>(bd.csel, 512)));
+  const int zcap = static_cast<int>(std::max<int64_t>(256, bd.csel));
   const size_t lds = recsa::attend_lds_bytes(static_cast<int>(I.d), static_cast<int>(I.G), static_cast<int>(bd.smax),
-                                             static_cast<int>(bd.csel), ch0);
+                                             zcap);
   if (lds > kMaxLds) return fail(RECSA_ERR_UNSUPPORTED, "needs %zu bytes of LDS (max %zu)", lds, kMaxLds);
   const int64_t need_ws = table_bytes(I, bd.P);
   if (ws_bytes < need_ws) return fail(RECSA_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes, (long long)need_ws);
@@ -224,8 +224,7 @@ int32_t run_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, const
   a.scale = I.scale;
   a.use_rope = I.theta != 0.0f;
   a.smax = static_cast<int32_t>(bd.smax);
-  a.csel = static_cast<int32_t>(bd.csel);
-  a.ch0 = ch0;
+  a.zcap = zcap;
   for (int lv = 1; lv <= RECSA_MAX_LEVELS; ++lv) a.k.k[lv] = lv <= n_levels ? k[lv - 1] : 0;
   const int Tc = levels_of(I.cap, I.f);
   for (int lv = 1; lv <= Tc && lv <= RECSA_MAX_LEVELS; ++lv) {

@@ -1,4 +1,4 @@
-// RecSA descent + one softmax, one workgroup per (sequence, query, KV head).
+// RecSA descent + one softmax: one wave (64 lanes) per (sequence, query, KV head).
 //
 // RecSA abstract ("Recursive Sparse Attention: Million-Token Length
 // Extrapolation at Logarithmic Cost"): a query keeps at most k candidates per
@@ -16,21 +16,21 @@
 //               storage type; the query heads rotated at C and rounded; the
 //               logit z = scale * <q~, k~> per head (float32, any order), the
 //               group score S = sum over the G heads of the KV group.
-//   select      the s = min(k, C) largest (S, -i) keys, by an 8-bit radix
-//               select over 64-bit keys in LDS (exact, deterministic).
+//   select      the s = min(k, C) largest (S, -i) keys: s rounds of a wave-wide
+//               64-bit max (exact, deterministic, lowest index wins ties).
 //   softmax     unkept candidates join the online softmax with their node's
 //               mean value; kept ones become the next level's parents.
 // Token level: the tokens under the kept level-1 nodes plus the trailing
 // partial block, all entries; the query sits at C_0, or C_0 - 1 when its own
 // token is one of them (causal prefill).
 //
-// Work layout (256 threads = 4 waves of 64):
-//   score phase  D/8 lanes per candidate row, 8 elements (16 B for bf16) per
-//                lane: one coalesced row load, the rotate-half partner via a
-//                lane shuffle, G partial dot products reduced by shuffles;
-//                the G query heads of the KV group share every loaded row.
-//   value phase  a wave per entry, D/64 dims per lane; every wave keeps a
-//                partial (acc) for all G heads; waves merge at the end.
+// A unit is a dependent chain of T + 1 rounds, so the kernel runs one wave per
+// unit with no workgroup barrier and lets many independent units share a CU.
+// Lane layout: D/8 lanes per candidate row; in the score phase a lane holds
+// elements [4s, 4s+4) and their rotate-half partners [D/2 + 4s, ...), so the
+// rotation needs no lane exchange; bf16 operands are rounded and packed by
+// v_cvt_pk_bf16_f32 and dotted by v_dot2 (the G query heads share each loaded
+// row); in the value phase a lane holds elements [8s, 8s+8).
 #include <math.h>
 
 #include "common.hpp"
@@ -38,37 +38,63 @@
 
 namespace recsa {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Round two floats to bf16 (nearest, ties to even) and pack them.
+__device__ __forceinline__ bf16x2_t pack_bf16_rne(float lo, float hi) {
+  return __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(v)), m));
+  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(v >> 32)), m));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// 4 consecutive storage elements -> float.
+template <bool BF16>
+__device__ __forceinline__ void load4(const void* base, int64_t off, float (&x)[4]) {
+  if constexpr (BF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
+    x[0] = __uint_as_float(u.x << 16);
+    x[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(u.y << 16);
+    x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+}
 
 struct Lds {
-  uint32_t qraw, qrot, selA, selB, zs, keys, flags, red, hist, nls, misc, fin, total;
+  uint32_t q, zs, sc, flags, selA, selB, nls, total;
 };
 
 __host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
 
-__host__ __device__ inline Lds lds_layout(int d, int G, int smax, int csel, int ch0) {
-  const uint32_t zcap = static_cast<uint32_t>(csel > ch0 ? csel : ch0);
+__host__ __device__ inline Lds lds_layout(int d, int G, int smax, int zcap) {
   Lds L;
   uint32_t o = 0;
-  L.qraw = o;  o = align16(o + 4u * G * d);
-  L.qrot = o;  o = align16(o + 4u * G * d);
-  L.selA = o;  o = align16(o + 4u * smax);
+  L.q = o;     o = align16(o + 4u * G * d);         // raw query heads of the KV group
+  L.zs = o;    o = align16(o + 4u * G * zcap);      // logits, then softmax weights, [G][zcap]
+  L.sc = o;    o = align16(o + 4u * zcap);          // group scores
+  L.flags = o; o = align16(o + zcap);               // kept flags
+  L.selA = o;  o = align16(o + 4u * smax);          // kept node ids, two buffers
   L.selB = o;  o = align16(o + 4u * smax);
-  L.zs = o;    o = align16(o + 4u * G * zcap);
-  L.keys = o;  o = align16(o + 8u * csel);
-  L.flags = o; o = align16(o + zcap);
-  L.red = o;   o = align16(o + 4u * 2 * kWaves * G);
-  L.hist = o;  o = align16(o + 4u * 256);
   L.nls = o;   o = align16(o + 8u * (RECSA_MAX_LEVELS + 2));
-  L.misc = o;  o = align16(o + 8u * 4);
-  L.fin = o;   o = align16(o + 4u * kWaves * G * d);
   L.total = o;
   return L;
 }
 
-size_t attend_lds_bytes(int d, int G, int smax, int csel, int ch0) {
-  return lds_layout(d, G, smax, csel, ch0).total;
+size_t attend_lds_bytes(int d, int G, int smax, int zcap) {
+  return lds_layout(d, G, smax, zcap).total;
 }
 
 // Candidate index -> node (or token) id: children of the kept parents, then orphans.
@@ -82,85 +108,26 @@ struct CandMap {
   }
 };
 
-// Exact top-s of C unique 64-bit keys: flags[i] = 1 for the s largest.
-__device__ void radix_select(const uint64_t* keys, int64_t C, int64_t s, uint8_t* flags,
-                             uint32_t* hist, uint64_t* misc) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint64_t prefix = 0, mask = 0;
-  int64_t need = s;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
-    for (int64_t i = tid; i < C; i += kThreads) {
-      const uint64_t k = keys[i];
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t c[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) c[q] = hist[255 - 4 * lane - q];  // descending digits
-      const uint32_t tot = c[0] + c[1] + c[2] + c[3];
-      uint32_t inc = tot;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = __shfl_up(inc, off);
-        if (lane >= off) inc += t;
-      }
-      const uint32_t exc = inc - tot;
-      if (static_cast<int64_t>(exc) < need && need <= static_cast<int64_t>(inc)) {
-        uint32_t cum = exc;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (static_cast<int64_t>(cum + c[q]) >= need) {
-            misc[0] = static_cast<uint64_t>(255 - 4 * lane - q);
-            misc[1] = cum;
-            misc[2] = c[q];
-            break;
-          }
-          cum += c[q];
-        }
-      }
-    }
-    __syncthreads();
-    const uint64_t digit = misc[0];
-    const int64_t above = static_cast<int64_t>(misc[1]);
-    const int64_t cnt = static_cast<int64_t>(misc[2]);
-    __syncthreads();
-    need -= above;
-    prefix |= digit << shift;
-    mask |= 0xFFull << shift;
-    if (cnt == need) break;  // every key left in this digit is kept
-  }
-  for (int64_t i = tid; i < C; i += kThreads) flags[i] = (keys[i] & mask) >= prefix ? 1 : 0;
-}
-
 template <int D, bool BF16, int G>
-__global__ __launch_bounds__(kThreads) void attend_kernel(AttnArgs a) {
-  constexpr int RL = D / 8;            // lanes per candidate row (score phase)
-  constexpr int RPW = kWave / RL;      // rows per wave
-  constexpr int RPI = RPW * kWaves;    // rows per iteration
-  constexpr int DPL = D / kWave;       // dims per lane (value phase)
+__global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
+  constexpr int RL = D / 8;            // lanes per row
+  constexpr int RPP = kWave / RL;      // rows per pass
   constexpr int HALF = D / 2;
-  constexpr int PV_UNROLL = 4;
+  constexpr int PV_UNROLL = 2;
 
   extern __shared__ __align__(16) unsigned char lds[];
-  const Lds L = lds_layout(D, G, a.smax, a.csel, a.ch0);
-  float* qraw = reinterpret_cast<float*>(lds + L.qraw);
-  float* qrot = reinterpret_cast<float*>(lds + L.qrot);
+  const int zcap = a.zcap;
+  const Lds L = lds_layout(D, G, a.smax, zcap);
+  float* qs = reinterpret_cast<float*>(lds + L.q);
+  float* zs = reinterpret_cast<float*>(lds + L.zs);
+  float* sc = reinterpret_cast<float*>(lds + L.sc);
+  uint8_t* flags = reinterpret_cast<uint8_t*>(lds + L.flags);
   int32_t* selA = reinterpret_cast<int32_t*>(lds + L.selA);
   int32_t* selB = reinterpret_cast<int32_t*>(lds + L.selB);
-  float* zs = reinterpret_cast<float*>(lds + L.zs);
-  uint64_t* keys = reinterpret_cast<uint64_t*>(lds + L.keys);
-  uint8_t* flags = reinterpret_cast<uint8_t*>(lds + L.flags);
-  float* red = reinterpret_cast<float*>(lds + L.red);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(lds + L.hist);
   int64_t* nls = reinterpret_cast<int64_t*>(lds + L.nls);
-  uint64_t* misc = reinterpret_cast<uint64_t*>(lds + L.misc);
-  float* fin = reinterpret_cast<float*>(lds + L.fin);
-  const int zcap = a.csel > a.ch0 ? a.csel : a.ch0;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
+  const int sub = lane % RL, rg = lane / RL;
   const int64_t unit = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int64_t j = unit / a.Hkv;
@@ -169,9 +136,16 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnArgs a) {
   const int f = a.f;
   const int64_t bh = b * a.Hkv + h;
 
-  const int64_t qbase = ((b * a.n_q + j) * a.Hq + static_cast<int64_t>(h) * G) * D;
-  for (int i = tid; i < G * D; i += kThreads) qraw[i] = load1<BF16>(a.q, qbase + i);
-  if (tid == 0) {
+  // raw query heads of the KV group -> LDS (float)
+  {
+    const int64_t qbase = ((b * a.n_q + j) * a.Hq + static_cast<int64_t>(h) * G) * D;
+    for (int i = lane * 4; i < G * D; i += kWave * 4) {
+      float x[4];
+      load4<BF16>(a.q, qbase + i, x);
+      *reinterpret_cast<float4*>(qs + i) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+  }
+  if (lane == 0) {
     int T = 0;
     int64_t m = n / f;
     while (m >= 1 && T < RECSA_MAX_LEVELS) {
@@ -181,91 +155,121 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnArgs a) {
     nls[T + 1] = 0;
     nls[0] = T;
   }
-  __syncthreads();
+  wave_sync();
   const int T = static_cast<int>(nls[0]);
   const int64_t sel_row0 = ((b * a.n_q + j) * a.Hkv + h) * a.n_levels;
   if (a.sel) {
     for (int lv = T + 1; lv <= a.n_levels; ++lv)
-      for (int c = tid; c < a.sel_width; c += kThreads) a.sel[(sel_row0 + lv - 1) * a.sel_width + c] = -1;
+      for (int c = lane; c < a.sel_width; c += kWave) a.sel[(sel_row0 + lv - 1) * a.sel_width + c] = -1;
   }
 
-  float m_run[G], l_run[G], acc[G][DPL];
+  float m_run[G], l_run[G], acc[G][8];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     m_run[hh] = -INFINITY;
     l_run[hh] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[hh][e] = 0.0f;
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
   }
 
-  // --- helpers over the current candidate map ---------------------------------
+  // rotated query operands for the current level
+  bf16x2_t qp[G][4];   // bf16: packed (lo0,lo1), (lo2,lo3), (hi0,hi1), (hi2,hi3)
+  float qf[G][8];      // f32: lo0..lo3, hi0..hi3
   auto rotate_query = [&](int64_t pos) {
-    for (int idx = tid; idx < G * HALF; idx += kThreads) {
-      const int hh = idx / HALF, i = idx % HALF;
-      const float x1 = qraw[hh * D + i], x2 = qraw[hh * D + i + HALF];
-      if (a.use_rope) {
-        const float2 cs = a.tab[pos * HALF + i];
-        const float p1 = x1 * cs.x, p2 = x2 * cs.y, p3 = x2 * cs.x, p4 = x1 * cs.y;
-        qrot[hh * D + i] = round_store<BF16>(p1 - p2);
-        qrot[hh * D + i + HALF] = round_store<BF16>(p3 + p4);
+    float c[4], s[4];
+    if (a.use_rope) {
+      const float4* t = reinterpret_cast<const float4*>(a.tab + pos * HALF + 4 * sub);
+      const float4 t0 = t[0], t1 = t[1];
+      c[0] = t0.x; s[0] = t0.y; c[1] = t0.z; s[1] = t0.w;
+      c[2] = t1.x; s[2] = t1.y; c[3] = t1.z; s[3] = t1.w;
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float4 xl = *reinterpret_cast<const float4*>(qs + hh * D + 4 * sub);
+      const float4 xh = *reinterpret_cast<const float4*>(qs + hh * D + HALF + 4 * sub);
+      const float ql[4] = {xl.x, xl.y, xl.z, xl.w}, qh[4] = {xh.x, xh.y, xh.z, xh.w};
+      float lo[4], hi[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (a.use_rope) {
+          const float p1 = ql[e] * c[e], p2 = qh[e] * s[e];
+          const float p3 = qh[e] * c[e], p4 = ql[e] * s[e];
+          lo[e] = p1 - p2;
+          hi[e] = p3 + p4;
+        } else {
+          lo[e] = ql[e];
+          hi[e] = qh[e];
+        }
+      }
+      if constexpr (BF16) {
+        qp[hh][0] = pack_bf16_rne(lo[0], lo[1]);
+        qp[hh][1] = pack_bf16_rne(lo[2], lo[3]);
+        qp[hh][2] = pack_bf16_rne(hi[0], hi[1]);
+        qp[hh][3] = pack_bf16_rne(hi[2], hi[3]);
       } else {
-        qrot[hh * D + i] = x1;
-        qrot[hh * D + i + HALF] = x2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qf[hh][e] = lo[e];
+          qf[hh][4 + e] = hi[e];
+        }
       }
     }
   };
 
-  // logits of candidates [c0, c0 + cn) (index = RoPE position) into zs[hh * zcap + r]
-  auto score_rows = [&](const void* src, int64_t rowbase, const CandMap& cm, int64_t c0, int64_t cn,
-                        bool want_keys) {
-    const int sub = lane % RL, rg = lane / RL;
-    float qv[G][8];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[hh][e] = qrot[hh * D + sub * 8 + e];
-    const int pi0 = (sub % (RL / 2)) * 8;
-    const bool first_half = sub < RL / 2;
-    for (int64_t r0 = 0; r0 < cn; r0 += RPI) {
-      const int64_t r = r0 + wave * RPW + rg;
+  // logits of candidates [c0, c0 + cn) (index = RoPE position) -> zs[hh * zcap + r], sc[r]
+  auto score_rows = [&](const void* src, int64_t rowbase, const CandMap& cm, int64_t c0, int64_t cn) {
+    for (int64_t r0 = 0; r0 < cn; r0 += RPP) {
+      const int64_t r = r0 + rg;
       const bool valid = r < cn;
       const int64_t i = c0 + r;
-      float x[8];
+      float klo[4], khi[4];
       if (valid) {
-        load8<BF16>(src, (rowbase + cm(i)) * D + sub * 8, x);
+        const int64_t off = (rowbase + cm(i)) * D + 4 * sub;
+        load4<BF16>(src, off, klo);
+        load4<BF16>(src, off + HALF, khi);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+        for (int e = 0; e < 4; ++e) { klo[e] = 0.0f; khi[e] = 0.0f; }
       }
-      float kx[8];
+      float olo[4], ohi[4];
       if (a.use_rope) {
-        float y[8];
+        const float4* t = reinterpret_cast<const float4*>(a.tab + (valid ? i : 0) * HALF + 4 * sub);
+        const float4 t0 = t[0], t1 = t[1];
+        const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = __shfl_xor(x[e], RL / 2);
-        const float4* t4 = reinterpret_cast<const float4*>(a.tab + (valid ? i : 0) * HALF + pi0);
-        float cs[16];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float4 t = t4[u];
-          cs[4 * u] = t.x; cs[4 * u + 1] = t.y; cs[4 * u + 2] = t.z; cs[4 * u + 3] = t.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
           const float c = cs[2 * e], s = cs[2 * e + 1];
-          const float p1 = x[e] * c, p2 = y[e] * s;
-          kx[e] = round_store<BF16>(first_half ? p1 - p2 : p1 + p2);
+          const float p1 = klo[e] * c, p2 = khi[e] * s;
+          const float p3 = khi[e] * c, p4 = klo[e] * s;
+          olo[e] = p1 - p2;
+          ohi[e] = p3 + p4;
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kx[e] = x[e];
+        for (int e = 0; e < 4; ++e) { olo[e] = klo[e]; ohi[e] = khi[e]; }
       }
       float part[G];
+      if constexpr (BF16) {
+        const bf16x2_t k0 = pack_bf16_rne(olo[0], olo[1]), k1 = pack_bf16_rne(olo[2], olo[3]);
+        const bf16x2_t k2 = pack_bf16_rne(ohi[0], ohi[1]), k3 = pack_bf16_rne(ohi[2], ohi[3]);
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float p = 0.0f;
+        for (int hh = 0; hh < G; ++hh) {
+          float p = __builtin_amdgcn_fdot2_f32_bf16(k0, qp[hh][0], 0.0f, false);
+          p = __builtin_amdgcn_fdot2_f32_bf16(k1, qp[hh][1], p, false);
+          p = __builtin_amdgcn_fdot2_f32_bf16(k2, qp[hh][2], p, false);
+          p = __builtin_amdgcn_fdot2_f32_bf16(k3, qp[hh][3], p, false);
+          part[hh] = p;
+        }
+      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p = fmaf(qv[hh][e], kx[e], p);
-        part[hh] = p;
+        for (int hh = 0; hh < G; ++hh) {
+          float p = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = fmaf(qf[hh][e], olo[e], p);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p = fmaf(qf[hh][4 + e], ohi[e], p);
+          part[hh] = p;
+        }
       }
 #pragma unroll
       for (int off = RL / 2; off >= 1; off >>= 1)
@@ -279,40 +283,60 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnArgs a) {
           zs[hh * zcap + r] = z;
           S = S + z;
         }
-        if (want_keys) keys[r] = select_key(S, static_cast<uint32_t>(i));
+        sc[r] = S;
       }
     }
+    wave_sync();
   };
 
-  // fold entries r in [0, cn) (skipping kept ones when use_flags) into the online softmax
+  // flags[r] = 1 for the s largest (S, -r) keys among r < C
+  auto select_top = [&](int64_t C, int64_t s) {
+    for (int64_t r = lane; r < C; r += kWave) flags[r] = 0;
+    wave_sync();
+    uint64_t best = 0;
+    int64_t slot = -1;
+    for (int64_t r = lane; r < C; r += kWave) {
+      const uint64_t k = select_key(sc[r], static_cast<uint32_t>(r));
+      if (k > best) { best = k; slot = r; }
+    }
+    for (int64_t it = 0; it < s; ++it) {
+      uint64_t w = best;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t o = shfl_xor_u64(w, off);
+        w = o > w ? o : w;
+      }
+      if (best == w) {            // keys are unique: exactly one lane holds the maximum
+        flags[slot] = 1;
+        best = 0;
+        slot = -1;
+        for (int64_t r = lane; r < C; r += kWave) {
+          if (flags[r]) continue;
+          const uint64_t k = select_key(sc[r], static_cast<uint32_t>(r));
+          if (k > best) { best = k; slot = r; }
+        }
+      }
+    }
+    wave_sync();
+  };
+
+  // fold entries r < cn (skipping kept ones when use_flags) into the online softmax
   auto softmax_pv = [&](const void* vsrc, int64_t rowbase, const CandMap& cm, int64_t c0, int64_t cn,
                         bool use_flags) {
-    float lm[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) lm[hh] = -INFINITY;
-    for (int64_t r = tid; r < cn; r += kThreads) {
-      if (use_flags && flags[r]) continue;
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) lm[hh] = fmaxf(lm[hh], zs[hh * zcap + r]);
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      lm[hh] = wave_max(lm[hh]);
-      if (lane == 0) red[wave * G + hh] = lm[hh];
-    }
-    __syncthreads();
     float mnew[G];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float mx = m_run[hh];
+    for (int hh = 0; hh < G; ++hh) mnew[hh] = -INFINITY;
+    for (int64_t r = lane; r < cn; r += kWave) {
+      if (use_flags && flags[r]) continue;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, red[w * G + hh]);
-      mnew[hh] = mx;
+      for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(mnew[hh], zs[hh * zcap + r]);
     }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(m_run[hh], wave_max(mnew[hh]));
     float ls[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) ls[hh] = 0.0f;
-    for (int64_t r = tid; r < cn; r += kThreads) {
+    for (int64_t r = lane; r < cn; r += kWave) {
       const bool skip = use_flags && flags[r];
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
@@ -323,45 +347,36 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      ls[hh] = wave_sum(ls[hh]);
-      if (lane == 0) red[(kWaves + wave) * G + hh] = ls[hh];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float lsum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) lsum += red[(kWaves + w) * G + hh];
+      const float lsum = wave_sum(ls[hh]);
       const float alpha = expf(m_run[hh] - mnew[hh]);
       l_run[hh] = l_run[hh] * alpha + lsum;
       m_run[hh] = mnew[hh];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[hh][e] *= alpha;
+      for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
     }
-    // value rows: a wave per entry, PV_UNROLL rows in flight
-    for (int64_t r0 = wave; r0 < cn; r0 += kWaves * PV_UNROLL) {
-      float v[PV_UNROLL][DPL];
+    wave_sync();
+    for (int64_t r0 = 0; r0 < cn; r0 += RPP * PV_UNROLL) {
+      float v[PV_UNROLL][8];
       bool live[PV_UNROLL];
 #pragma unroll
       for (int u = 0; u < PV_UNROLL; ++u) {
-        const int64_t r = r0 + u * kWaves;
+        const int64_t r = r0 + u * RPP + rg;
         live[u] = r < cn && !(use_flags && flags[r]);
-        if (live[u]) {
-          loadN<BF16, DPL>(vsrc, (rowbase + cm(c0 + r)) * D + lane * DPL, v[u]);
-        }
+        if (live[u]) load8<BF16>(vsrc, (rowbase + cm(c0 + r)) * D + 8 * sub, v[u]);
       }
 #pragma unroll
       for (int u = 0; u < PV_UNROLL; ++u) {
         if (!live[u]) continue;
-        const int64_t r = r0 + u * kWaves;
+        const int64_t r = r0 + u * RPP + rg;
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
           const float p = zs[hh * zcap + r];
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[hh][e] = fmaf(p, v[u][e], acc[hh][e]);
+          for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(p, v[u][e], acc[hh][e]);
         }
       }
     }
+    wave_sync();
   };
 
   // --- levels T .. 1 -------------------------------------------------------------
@@ -375,42 +390,38 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnArgs a) {
     const int64_t kl = a.k.k[lv];
     const int64_t s = kl < C ? kl : C;
     if (s == C) {
-      for (int64_t i = tid; i < C; i += kThreads) sel_new[i] = static_cast<int32_t>(cm(i));
+      for (int64_t i = lane; i < C; i += kWave) sel_new[i] = static_cast<int32_t>(cm(i));
+      wave_sync();
     } else {
       const int64_t rowbase = bh * a.tree.rows[lv];
       rotate_query(C);
-      __syncthreads();
-      score_rows(a.tree.NK[lv], rowbase, cm, 0, C, s > 0);
-      __syncthreads();
+      score_rows(a.tree.NK[lv], rowbase, cm, 0, C);
       if (s > 0) {
-        radix_select(keys, C, s, flags, hist, misc);
+        select_top(C, s);
       } else {
-        for (int64_t i = tid; i < C; i += kThreads) flags[i] = 0;
+        for (int64_t r = lane; r < C; r += kWave) flags[r] = 0;
+        wave_sync();
       }
-      __syncthreads();
-      if (wave == 0) {
-        int64_t cnt = 0;
-        for (int64_t base = 0; base < C; base += kWave) {
-          const int64_t i = base + lane;
-          const bool fl = i < C && flags[i];
-          const uint64_t bal = __ballot(fl);
-          const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-          if (fl) sel_new[cnt + pre] = static_cast<int32_t>(cm(i));
-          cnt += __popcll(bal);
-        }
+      int64_t cnt = 0;
+      for (int64_t base = 0; base < C; base += kWave) {
+        const int64_t i = base + lane;
+        const bool fl = i < C && flags[i];
+        const uint64_t bal = __ballot(fl);
+        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+        if (fl) sel_new[cnt + pre] = static_cast<int32_t>(cm(i));
+        cnt += __popcll(bal);
       }
+      wave_sync();
       softmax_pv(a.tree.NV[lv], rowbase, cm, 0, C, true);
     }
-    __syncthreads();
     if (a.sel) {
-      for (int c = tid; c < a.sel_width; c += kThreads)
+      for (int c = lane; c < a.sel_width; c += kWave)
         a.sel[(sel_row0 + lv - 1) * a.sel_width + c] = c < s ? sel_new[c] : -1;
     }
     int32_t* t = sel_prev;
     sel_prev = sel_new;
     sel_new = t;
     s_prev = s;
-    __syncthreads();
   }
 
   // --- token level -------------------------------------------------------------------
@@ -421,40 +432,36 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnArgs a) {
     const bool own = a.prefill && C0 > 0 && cm(C0 - 1) == n - 1;
     const int64_t pq = own ? C0 - 1 : C0;
     const int64_t rowbase = bh * a.cap;
-    if (C0 > 0) {
-      rotate_query(pq);
-      __syncthreads();
-    }
-    for (int64_t c0 = 0; c0 < C0; c0 += a.ch0) {
-      const int64_t cn = C0 - c0 < a.ch0 ? C0 - c0 : a.ch0;
-      score_rows(a.K, rowbase, cm, c0, cn, false);
-      __syncthreads();
+    if (C0 > 0) rotate_query(pq);
+    for (int64_t c0 = 0; c0 < C0; c0 += zcap) {
+      const int64_t cn = C0 - c0 < zcap ? C0 - c0 : zcap;
+      score_rows(a.K, rowbase, cm, c0, cn);
       softmax_pv(a.V, rowbase, cm, c0, cn, false);
-      __syncthreads();
     }
   }
 
-  // --- merge the waves' partial sums, normalise, write -----------------------------
+  // --- merge the row groups' partial sums, normalise, write ---------------------------
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+  for (int off = RL; off < kWave; off <<= 1)
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) fin[(wave * G + hh) * D + lane * DPL + e] = acc[hh][e];
-  __syncthreads();
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], off);
   const int64_t obase = ((b * a.n_q + j) * a.Hq + static_cast<int64_t>(h) * G) * D;
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int hh = idx / D;
-    float sum = 0.0f;
+  if (rg == 0) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) sum += fin[(w * G) * D + idx];
-    float l = 0.0f;
-#pragma unroll
-    for (int g2 = 0; g2 < G; ++g2) l = (g2 == hh) ? l_run[g2] : l;
-    a.out[obase + idx] = l > 0.0f ? sum / l : 0.0f;
+    for (int hh = 0; hh < G; ++hh) {
+      const float l = l_run[hh];
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      float4* o = reinterpret_cast<float4*>(a.out + obase + hh * D + 8 * sub);
+      o[0] = make_float4(acc[hh][0] * inv, acc[hh][1] * inv, acc[hh][2] * inv, acc[hh][3] * inv);
+      o[1] = make_float4(acc[hh][4] * inv, acc[hh][5] * inv, acc[hh][6] * inv, acc[hh][7] * inv);
+    }
   }
   if (a.lse) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      if (tid == hh) {
+      if (lane == hh) {
         a.lse[(b * a.n_q + j) * a.Hq + static_cast<int64_t>(h) * G + hh] =
             l_run[hh] > 0.0f ? m_run[hh] + logf(l_run[hh]) : -INFINITY;
       }
@@ -465,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnArgs a) {
 template <int D, bool BF16, int G>
 static hipError_t launch_attend_t(const AttnArgs& a, size_t lds, int64_t B, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.n_q * a.Hkv), static_cast<unsigned>(B));
-  hipLaunchKernelGGL((attend_kernel<D, BF16, G>), grid, dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((attend_kernel<D, BF16, G>), grid, dim3(kWave), lds, s, a);
   return hipGetLastError();
 }
 

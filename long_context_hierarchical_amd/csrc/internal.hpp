@@ -60,13 +60,12 @@ struct AttnArgs {
   float scale;
   int32_t use_rope;
   int32_t smax;         // capacity of a kept-node list
-  int32_t csel;         // capacity of a scored candidate list at a selecting level
-  int32_t ch0;          // token-level chunk
+  int32_t zcap;         // capacity of a scored candidate list (selecting levels and token-level chunks)
   LevelK k;
   TreeLevels tree;
 };
 
-size_t attend_lds_bytes(int d, int G, int smax, int csel, int ch0);
+size_t attend_lds_bytes(int d, int G, int smax, int zcap);
 hipError_t launch_attend(const AttnArgs& a, int d, bool bf16, int G, size_t lds, int64_t B, hipStream_t s);
 
 }  // namespace recsa
