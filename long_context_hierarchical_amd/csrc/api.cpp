@@ -304,29 +304,40 @@ int32_t recsa_build_tree(const recsa_shape_t* shape, const void* K, const void* 
   if (!aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(tree))
     return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  for (int lv = 1; lv <= T; ++lv) {
+  const int Tc = levels_of(I.cap, I.f);
+  const bool can_fuse = I.f == recsa::pool_nodes_per_tile(static_cast<int>(I.d));
+  for (int lv = 1; lv <= T;) {
     const int64_t lo = nodes_at(n_old, I.f, lv), hi = nodes_at(n_new, I.f, lv);
-    if (hi <= lo) continue;
-    recsa::PoolArgs p{};
-    if (lv == 1) {
-      p.srcK = K;
-      p.srcV = V;
-      p.src_rows = I.cap;
-    } else {
-      p.srcK = static_cast<const char*>(tree) + level_offset_bytes(I, lv - 1, 0);
-      p.srcV = static_cast<const char*>(tree) + level_offset_bytes(I, lv - 1, 1);
-      p.src_rows = nodes_at(I.cap, I.f, lv - 1);
+    const bool fuse = can_fuse && lv + 1 <= Tc;
+    if (hi > lo) {
+      recsa::PoolArgs p{};
+      if (lv == 1) {
+        p.srcK = K;
+        p.srcV = V;
+        p.src_rows = I.cap;
+      } else {
+        p.srcK = static_cast<const char*>(tree) + level_offset_bytes(I, lv - 1, 0);
+        p.srcV = static_cast<const char*>(tree) + level_offset_bytes(I, lv - 1, 1);
+        p.src_rows = nodes_at(I.cap, I.f, lv - 1);
+      }
+      p.dstK = static_cast<char*>(tree) + level_offset_bytes(I, lv, 0);
+      p.dstV = static_cast<char*>(tree) + level_offset_bytes(I, lv, 1);
+      p.dst_rows = nodes_at(I.cap, I.f, lv);
+      p.W = W;
+      p.g_lo = lo;
+      p.g_hi = hi;
+      p.f = static_cast<int32_t>(I.f);
+      p.BH = static_cast<int32_t>(I.B * I.Hkv);
+      if (fuse) {
+        p.fuse_next = 1;
+        p.dst2K = static_cast<char*>(tree) + level_offset_bytes(I, lv + 1, 0);
+        p.dst2V = static_cast<char*>(tree) + level_offset_bytes(I, lv + 1, 1);
+        p.dst2_rows = nodes_at(I.cap, I.f, lv + 1);
+      }
+      hipError_t e = recsa::launch_pool_level(p, static_cast<int>(I.d), I.bf16, st);
+      if (e != hipSuccess) return hip_fail(e, "tree build launch");
     }
-    p.dstK = static_cast<char*>(tree) + level_offset_bytes(I, lv, 0);
-    p.dstV = static_cast<char*>(tree) + level_offset_bytes(I, lv, 1);
-    p.dst_rows = nodes_at(I.cap, I.f, lv);
-    p.W = W;
-    p.g_lo = lo;
-    p.g_hi = hi;
-    p.f = static_cast<int32_t>(I.f);
-    p.BH = static_cast<int32_t>(I.B * I.Hkv);
-    hipError_t e = recsa::launch_pool_level(p, static_cast<int>(I.d), I.bf16, st);
-    if (e != hipSuccess) return hip_fail(e, "tree build launch");
+    lv += fuse ? 2 : 1;
   }
   return RECSA_OK;
 }

@@ -32,8 +32,8 @@ RoPE with fp32 inverse frequencies; scale 1/sqrt(d); no size bias.
 Precision. Steps whose rounding decides a selection follow the kernel's
 precision with explicit rounding points, so both sides take each decision on
 the same numbers: node sums in float32 in child order, divided by f, the
-pooler's product accumulated in float32 input by input with separate
-multiply and add, results rounded to the storage type; the rotation with
+pooler's product accumulated in float32 input by input with one fused
+multiply-add (one rounding) per term, results rounded to the storage type; the rotation with
 separate multiply and add, rounded to the storage type; the logit is the
 float64 dot product of the rounded operands times the float32 scale,
 rounded once to float32. The group score, the softmax and the weighted value
@@ -129,24 +129,15 @@ def pool_nodes(cK: np.ndarray, cV: np.ndarray, W: np.ndarray, f: int, dtype: str
     f child keys; value = mean of the f stored child values (equal to the
     subtree mean for a complete subtree).
 
+    Arithmetic (oracle/csrc/pool.c, plain C): child sums in float32 in child
+    order, one division by f, then key_i accumulated over j = 0..d-1 as
+    acc = fmaf(W[i][j], m[j], acc) (one rounding per term), rounded to the
+    storage type.
+
     cK, cV: [g, f, d] float32; W: [d, d] float32 (key_i = sum_j W[i, j] m_j).
     """
-    g, _, d = cK.shape
-    a = np.zeros((g, d), _F32)
-    for j in range(f):                       # child order, float32 adds
-        a = a + cK[:, j, :]
-    m = a / _F32(f)
-    acc = np.zeros((g, d), _F32)
-    prod = np.empty((g, d), _F32)
-    for jj in range(d):                      # input order, separate multiply and add
-        np.multiply(W[None, :, jj], m[:, jj, None], out=prod)
-        np.add(acc, prod, out=acc)
-    NK = round_store(acc, dtype)
-    b = np.zeros((g, d), _F32)
-    for j in range(f):
-        b = b + cV[:, j, :]
-    NV = round_store(b / _F32(f), dtype)
-    return NK, NV
+    from . import _native
+    return _native.pool(cK, cV, W, f, dtype == "bf16")
 
 
 def build_slice(K: np.ndarray, V: np.ndarray, W: np.ndarray, f: int, dtype: str,

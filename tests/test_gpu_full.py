@@ -1,0 +1,129 @@
+"""GPU parity at the full workload sizes (131K-2M tokens), in the launch configuration the
+benchmark times: the whole workload runs on the GPU, the oracle checks sampled units (and, for
+the tree, whole (sequence, KV head) slices bit for bit)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, Gpu, compare_unit, storage_bits
+from long_context_hierarchical_amd import recsa as R
+from synthetic import WORKLOADS, gen_kv_slice, gen_queries, gen_W
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _upload_workload(w, n_q):
+    """K, V, q for the whole workload straight to the device, slice by slice; host keeps q only."""
+    dev = "cuda:0"
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    K = torch.empty(w.B, w.Hkv, w.L, w.d, dtype=td, device=dev)
+    V = torch.empty_like(K)
+    qs = []
+    for b in range(w.B):
+        qb = gen_queries(w, b, n_q)
+        qs.append(qb)
+        for h in range(w.Hkv):
+            Kb, Vb = gen_kv_slice(w, b, h, qb)
+            K[b, h] = torch.from_numpy(Kb).view(td).to(dev)
+            V[b, h] = torch.from_numpy(Vb).view(td).to(dev)
+    q = np.stack(qs)
+    qd = torch.from_numpy(q).view(td).to(dev)
+    W = gen_W(w)
+    Wd = torch.from_numpy(W).view(td).to(dev)
+    return K, V, qd, Wd, q, W
+
+
+@pytest.mark.parametrize("name,n_q,units", [
+    ("c1", 256, [(0, 0, 0), (0, 17, 3), (0, 100, 7), (0, 255, 5), (0, 3, 1), (0, 64, 2)]),
+    ("c2", 256, [(0, 0, 0), (1, 5, 4), (2, 77, 7), (3, 255, 1), (3, 128, 6)]),
+    ("c4", 256, [(0, 0, 0), (0, 200, 5), (0, 31, 2), (0, 255, 7)]),
+])
+def test_full_size_decode(name, n_q, units):
+    w = WORKLOADS[name]
+    _say(f"full decode {name}: generating")
+    K, V, qd, Wd, q, W = _upload_workload(w, n_q)
+    sh = R.Shape(w.B, w.Hkv, w.Hq, w.d, w.f, w.dtype, w.L, 0.0, w.theta)
+    tree = torch.zeros(R.recsa_tree_bytes(sh), dtype=torch.uint8, device="cuda:0")
+    R.recsa_build_tree(sh, K, V, Wd, 0, w.L, tree)
+    T = R.recsa_num_levels(w.L, w.f)
+    k = [w.k] * T
+    width = R.recsa_sel_width(sh, w.L, w.L, k)
+    ws = torch.zeros(R.recsa_workspace_bytes(sh, w.L, k), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty(w.B, n_q, w.Hq, w.d, dtype=torch.float32, device="cuda:0")
+    lse = torch.empty(w.B, n_q, w.Hq, dtype=torch.float32, device="cuda:0")
+    sel = torch.empty(w.B, n_q, w.Hkv, T, width, dtype=torch.int32, device="cuda:0")
+    R.recsa_decode(sh, qd, K, V, tree, w.L, k, out, lse, sel, width, ws)
+    torch.cuda.synchronize()
+    _say(f"full decode {name}: gpu done, checking {len(units)} units")
+    out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
+    Wf = oracle.from_storage(W, w.dtype)
+    G = w.G
+    checked = {}
+    stats = {"match": 0, "excused": 0}
+    for (b, j, h) in units:
+        if (b, h) not in checked:
+            Kb, Vb = gen_kv_slice(w, b, h, q[b])
+            Kf, Vf = oracle.from_storage(Kb, w.dtype), oracle.from_storage(Vb, w.dtype)
+            tr = oracle.build_slice(Kf, Vf, Wf, w.f, w.dtype, n_new=w.L)
+            # the GPU's tree for this slice, bit for bit, every level
+            for lv in range(1, T + 1):
+                NK, NV = R.tree_level_views(sh, tree, lv)
+                for arr, ref in ((NK, tr[lv - 1][0]), (NV, tr[lv - 1][1])):
+                    got = storage_bits(arr[b, h])
+                    assert np.array_equal(got, oracle.to_storage(ref, w.dtype).view(got.dtype)), (b, h, lv)
+            checked[(b, h)] = (Kf, Vf, tr)
+        Kf, Vf, tr = checked[(b, h)]
+        qg = oracle.from_storage(q[b, j, h * G:(h + 1) * G], w.dtype)
+        r = oracle.attend_unit(qg, Kf, Vf, tr, w.L, w.f, k, w.dtype, w.theta)
+        st = compare_unit(r, sel[b, j, h], out[b, j, h * G:(h + 1) * G], lse[b, j, h * G:(h + 1) * G],
+                          TOL[w.dtype], where=f"{name} unit {(b, j, h)}")
+        stats[st] += 1
+    _say(f"full decode {name}: {stats}")
+    assert stats["match"] >= len(units) - 1
+
+
+def test_full_size_chunked_prefill_64k():
+    """64K-position causal prefill in chunks of 4096 with the tree extended chunk by chunk."""
+    w = WORKLOADS["c3"]
+    _say("full prefill c3: generating")
+    K, V, qd, Wd, q, W = _upload_workload(w, w.L)
+    sh = R.Shape(w.B, w.Hkv, w.Hq, w.d, w.f, w.dtype, w.L, 0.0, w.theta)
+    tree = torch.zeros(R.recsa_tree_bytes(sh), dtype=torch.uint8, device="cuda:0")
+    T = R.recsa_num_levels(w.L, w.f)
+    k = [w.k] * T
+    width = R.recsa_sel_width(sh, 1, w.L, k)
+    ws = torch.zeros(R.recsa_workspace_bytes(sh, w.L, k), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty(w.B, w.L, w.Hq, w.d, dtype=torch.float32, device="cuda:0")
+    lse = torch.empty(w.B, w.L, w.Hq, dtype=torch.float32, device="cuda:0")
+    sel = torch.empty(w.B, w.L, w.Hkv, T, width, dtype=torch.int32, device="cuda:0")
+    for c0 in range(0, w.L, w.chunk):
+        R.recsa_build_tree(sh, K, V, Wd, c0, c0 + w.chunk, tree)
+        R.recsa_prefill(sh, qd[:, c0:c0 + w.chunk], c0, K, V, tree, k, out[:, c0:c0 + w.chunk],
+                        lse[:, c0:c0 + w.chunk], sel[:, c0:c0 + w.chunk], width, ws)
+    torch.cuda.synchronize()
+    out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
+    rng = np.random.default_rng(5)
+    pos = sorted(set([0, 15, 16, 4095, 4096, 4097, 65535, 32768, 255, 256] + rng.integers(0, w.L, 14).tolist()))
+    units = [(0, p, int(rng.integers(0, w.Hkv))) for p in pos]
+    Wf = oracle.from_storage(W, w.dtype)
+    slices = {}
+    stats = {"match": 0, "excused": 0}
+    G = w.G
+    for (b, p, h) in units:
+        if h not in slices:
+            Kb, Vb = gen_kv_slice(w, b, h, q[b])
+            Kf, Vf = oracle.from_storage(Kb, w.dtype), oracle.from_storage(Vb, w.dtype)
+            slices[h] = (Kf, Vf, oracle.build_slice(Kf, Vf, Wf, w.f, w.dtype, n_new=w.L))
+        Kf, Vf, tr = slices[h]
+        qg = oracle.from_storage(q[b, p, h * G:(h + 1) * G], w.dtype)
+        r = oracle.attend_unit(qg, Kf, Vf, tr, p + 1, w.f, k, w.dtype, w.theta, self_in=True)
+        st = compare_unit(r, sel[b, p, h], out[b, p, h * G:(h + 1) * G], lse[b, p, h * G:(h + 1) * G],
+                          TOL[w.dtype], where=f"c3 position {p} head {h}")
+        stats[st] += 1
+    _say(f"full prefill c3: {stats}")
+    assert stats["match"] >= len(units) - 1

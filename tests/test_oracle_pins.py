@@ -347,3 +347,55 @@ def test_planted_needles_are_exact_entries():
         r = attend_unit(q, K, V, tree, n, f, [k] * 3, "f32", 0.0)
         toks = {i for lv, i in r.entries if lv == 0}
         assert set(plan[j]) <= toks, (j, plan[j])
+
+
+# ------------------------------------------------------------------ pooler arithmetic, exactly
+
+def _rn32(x):
+    """Correctly rounded float32 of an exact rational (ties to even)."""
+    from fractions import Fraction
+    y = np.float32(float(x))
+    cands = {float(y), float(np.nextafter(y, np.float32(np.inf))), float(np.nextafter(y, np.float32(-np.inf)))}
+
+    def key(c):
+        return (abs(Fraction(c) - x), int(np.float32(c).view(np.uint32)) & 1)
+    return np.float32(min(cands, key=key))
+
+
+@pytest.mark.parametrize("f,d,seed", [(2, 8, 0), (3, 8, 1), (16, 8, 2), (5, 16, 3)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pooler_follows_its_rounding_exactly(f, d, seed, dtype):
+    """Node keys and values against exact rational arithmetic rounded to float32 at each stated
+    point: child sums in child order, one division by f, one rounding per W[i][j] * m[j] + acc
+    term, then the storage rounding (torch's bfloat16 conversion for bf16)."""
+    from fractions import Fraction
+    from oracle.recsa import pool_nodes
+    rng = np.random.default_rng(seed)
+    g = 3
+    cK = _rand(rng, (g, f, d), 1.0, dtype)
+    cV = _rand(rng, (g, f, d), 1.0, dtype)
+    cK[0, 0, :2] = np.float32([1.0 + 2.0 ** -23, -3.0e-5])       # awkward magnitudes
+    cK = bf16_value(bf16_bits(cK)) if dtype == "bf16" else cK
+    W = _rand(rng, (d, d), 1.0, dtype)
+    NK, NV = pool_nodes(cK, cV, W, f, dtype)
+
+    def store(v):
+        v = np.float32(v)
+        if dtype == "bf16":
+            return torch.tensor([v], dtype=torch.float32).to(torch.bfloat16).to(torch.float32).numpy()[0]
+        return v
+
+    for n in range(g):
+        m = []
+        for j in range(d):
+            a, b = np.float32(0), np.float32(0)
+            for c in range(f):
+                a = _rn32(Fraction(float(a)) + Fraction(float(cK[n, c, j])))
+                b = _rn32(Fraction(float(b)) + Fraction(float(cV[n, c, j])))
+            m.append(_rn32(Fraction(float(a)) / f))
+            assert store(_rn32(Fraction(float(b)) / f)).view(np.uint32) == NV[n, j].view(np.uint32), (n, j)
+        for i in range(d):
+            acc = np.float32(0)
+            for j in range(d):
+                acc = _rn32(Fraction(float(W[i, j])) * Fraction(float(m[j])) + Fraction(float(acc)))
+            assert store(acc).view(np.uint32) == NK[n, i].view(np.uint32), (n, i)
