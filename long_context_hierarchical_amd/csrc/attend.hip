@@ -26,11 +26,12 @@
 //
 // A unit is a dependent chain of T + 1 rounds, so the kernel runs one wave per
 // unit with no workgroup barrier and lets many independent units share a CU.
-// Lane layout: D/8 lanes per candidate row; in the score phase a lane holds
-// elements [4s, 4s+4) and their rotate-half partners [D/2 + 4s, ...), so the
-// rotation needs no lane exchange; bf16 operands are rounded and packed by
-// v_cvt_pk_bf16_f32 and dotted by v_dot2 (the G query heads share each loaded
-// row); in the value phase a lane holds elements [8s, 8s+8).
+// Lane layout: in the score phase D/16 lanes per candidate row, a lane holding
+// elements [8s, 8s+8) and their rotate-half partners [D/2 + 8s, ...), so the
+// rotation needs no lane exchange and the per-row reduction is 3 (d=128)
+// shuffle steps; bf16 operands are rounded and packed by v_cvt_pk_bf16_f32 and
+// dotted by v_dot2 (the G query heads share each loaded row). In the value
+// phase D/8 lanes per row, a lane holding elements [8s, 8s+8).
 #include <math.h>
 
 #include "common.hpp"
@@ -110,8 +111,10 @@ struct CandMap {
 
 template <int D, bool BF16, int G>
 __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
-  constexpr int RL = D / 8;            // lanes per row
-  constexpr int RPP = kWave / RL;      // rows per pass
+  constexpr int RL = D / 8;            // lanes per row, value phase (8 elements per lane)
+  constexpr int RPP = kWave / RL;      // rows per pass, value phase
+  constexpr int SL = D / 16;           // lanes per row, score phase (8 rotate-half pairs per lane)
+  constexpr int SPP = kWave / SL;      // rows per pass, score phase
   constexpr int HALF = D / 2;
   constexpr int PV_UNROLL = 2;
 
@@ -127,7 +130,8 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
   int64_t* nls = reinterpret_cast<int64_t*>(lds + L.nls);
 
   const int lane = threadIdx.x;
-  const int sub = lane % RL, rg = lane / RL;
+  const int sub = lane % RL, rg = lane / RL;       // value phase
+  const int ssub = lane % SL, srg = lane / SL;     // score phase
   const int64_t unit = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int64_t j = unit / a.Hkv;
@@ -172,25 +176,33 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
   }
 
-  // rotated query operands for the current level
-  bf16x2_t qp[G][4];   // bf16: packed (lo0,lo1), (lo2,lo3), (hi0,hi1), (hi2,hi3)
-  float qf[G][8];      // f32: lo0..lo3, hi0..hi3
+  // rotated query operands for the current level: this lane's 8 rotate-half pairs
+  // (elements 8*ssub + e and HALF + 8*ssub + e, e < 8) of every head
+  bf16x2_t qp[G][8];   // bf16: packed (lo0,lo1), (lo2,lo3), .., (hi6,hi7)
+  float qf[G][16];     // f32: lo0..lo7, hi0..hi7
   auto rotate_query = [&](int64_t pos) {
-    float c[4], s[4];
+    float c[8], s[8];
     if (a.use_rope) {
-      const float4* t = reinterpret_cast<const float4*>(a.tab + pos * HALF + 4 * sub);
-      const float4 t0 = t[0], t1 = t[1];
-      c[0] = t0.x; s[0] = t0.y; c[1] = t0.z; s[1] = t0.w;
-      c[2] = t1.x; s[2] = t1.y; c[3] = t1.z; s[3] = t1.w;
+      const float4* t = reinterpret_cast<const float4*>(a.tab + pos * HALF + 8 * ssub);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 tv = t[u];
+        c[2 * u] = tv.x; s[2 * u] = tv.y; c[2 * u + 1] = tv.z; s[2 * u + 1] = tv.w;
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float4 xl = *reinterpret_cast<const float4*>(qs + hh * D + 4 * sub);
-      const float4 xh = *reinterpret_cast<const float4*>(qs + hh * D + HALF + 4 * sub);
-      const float ql[4] = {xl.x, xl.y, xl.z, xl.w}, qh[4] = {xh.x, xh.y, xh.z, xh.w};
-      float lo[4], hi[4];
+      float ql[8], qh[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int u = 0; u < 2; ++u) {
+        const float4 xl = *reinterpret_cast<const float4*>(qs + hh * D + 8 * ssub + 4 * u);
+        const float4 xh = *reinterpret_cast<const float4*>(qs + hh * D + HALF + 8 * ssub + 4 * u);
+        ql[4 * u] = xl.x; ql[4 * u + 1] = xl.y; ql[4 * u + 2] = xl.z; ql[4 * u + 3] = xl.w;
+        qh[4 * u] = xh.x; qh[4 * u + 1] = xh.y; qh[4 * u + 2] = xh.z; qh[4 * u + 3] = xh.w;
+      }
+      float lo[8], hi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
         if (a.use_rope) {
           const float p1 = ql[e] * c[e], p2 = qh[e] * s[e];
           const float p3 = qh[e] * c[e], p4 = ql[e] * s[e];
@@ -202,15 +214,16 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
         }
       }
       if constexpr (BF16) {
-        qp[hh][0] = pack_bf16_rne(lo[0], lo[1]);
-        qp[hh][1] = pack_bf16_rne(lo[2], lo[3]);
-        qp[hh][2] = pack_bf16_rne(hi[0], hi[1]);
-        qp[hh][3] = pack_bf16_rne(hi[2], hi[3]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          qp[hh][u] = pack_bf16_rne(lo[2 * u], lo[2 * u + 1]);
+          qp[hh][4 + u] = pack_bf16_rne(hi[2 * u], hi[2 * u + 1]);
+        }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 8; ++e) {
           qf[hh][e] = lo[e];
-          qf[hh][4 + e] = hi[e];
+          qf[hh][8 + e] = hi[e];
         }
       }
     }
@@ -218,46 +231,52 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
 
   // logits of candidates [c0, c0 + cn) (index = RoPE position) -> zs[hh * zcap + r], sc[r]
   auto score_rows = [&](const void* src, int64_t rowbase, const CandMap& cm, int64_t c0, int64_t cn) {
-    for (int64_t r0 = 0; r0 < cn; r0 += RPP) {
-      const int64_t r = r0 + rg;
+    for (int64_t r0 = 0; r0 < cn; r0 += SPP) {
+      const int64_t r = r0 + srg;
       const bool valid = r < cn;
       const int64_t i = c0 + r;
-      float klo[4], khi[4];
+      float klo[8], khi[8];
       if (valid) {
-        const int64_t off = (rowbase + cm(i)) * D + 4 * sub;
-        load4<BF16>(src, off, klo);
-        load4<BF16>(src, off + HALF, khi);
+        const int64_t off = (rowbase + cm(i)) * D + 8 * ssub;
+        load8<BF16>(src, off, klo);
+        load8<BF16>(src, off + HALF, khi);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { klo[e] = 0.0f; khi[e] = 0.0f; }
+        for (int e = 0; e < 8; ++e) { klo[e] = 0.0f; khi[e] = 0.0f; }
       }
-      float olo[4], ohi[4];
+      float olo[8], ohi[8];
       if (a.use_rope) {
-        const float4* t = reinterpret_cast<const float4*>(a.tab + (valid ? i : 0) * HALF + 4 * sub);
-        const float4 t0 = t[0], t1 = t[1];
-        const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+        const float4* t = reinterpret_cast<const float4*>(a.tab + (valid ? i : 0) * HALF + 8 * ssub);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float c = cs[2 * e], s = cs[2 * e + 1];
-          const float p1 = klo[e] * c, p2 = khi[e] * s;
-          const float p3 = khi[e] * c, p4 = klo[e] * s;
-          olo[e] = p1 - p2;
-          ohi[e] = p3 + p4;
+        for (int u = 0; u < 4; ++u) {
+          const float4 tv = t[u];
+          const float cc[2] = {tv.x, tv.z}, ss[2] = {tv.y, tv.w};
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+            const int e = 2 * u + v;
+            const float p1 = klo[e] * cc[v], p2 = khi[e] * ss[v];
+            const float p3 = khi[e] * cc[v], p4 = klo[e] * ss[v];
+            olo[e] = p1 - p2;
+            ohi[e] = p3 + p4;
+          }
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { olo[e] = klo[e]; ohi[e] = khi[e]; }
+        for (int e = 0; e < 8; ++e) { olo[e] = klo[e]; ohi[e] = khi[e]; }
       }
       float part[G];
       if constexpr (BF16) {
-        const bf16x2_t k0 = pack_bf16_rne(olo[0], olo[1]), k1 = pack_bf16_rne(olo[2], olo[3]);
-        const bf16x2_t k2 = pack_bf16_rne(ohi[0], ohi[1]), k3 = pack_bf16_rne(ohi[2], ohi[3]);
+        bf16x2_t kp[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          kp[u] = pack_bf16_rne(olo[2 * u], olo[2 * u + 1]);
+          kp[4 + u] = pack_bf16_rne(ohi[2 * u], ohi[2 * u + 1]);
+        }
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          float p = __builtin_amdgcn_fdot2_f32_bf16(k0, qp[hh][0], 0.0f, false);
-          p = __builtin_amdgcn_fdot2_f32_bf16(k1, qp[hh][1], p, false);
-          p = __builtin_amdgcn_fdot2_f32_bf16(k2, qp[hh][2], p, false);
-          p = __builtin_amdgcn_fdot2_f32_bf16(k3, qp[hh][3], p, false);
+          float p = 0.0f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) p = __builtin_amdgcn_fdot2_f32_bf16(kp[u], qp[hh][u], p, false);
           part[hh] = p;
         }
       } else {
@@ -265,17 +284,17 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
         for (int hh = 0; hh < G; ++hh) {
           float p = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) p = fmaf(qf[hh][e], olo[e], p);
+          for (int e = 0; e < 8; ++e) p = fmaf(qf[hh][e], olo[e], p);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) p = fmaf(qf[hh][4 + e], ohi[e], p);
+          for (int e = 0; e < 8; ++e) p = fmaf(qf[hh][8 + e], ohi[e], p);
           part[hh] = p;
         }
       }
 #pragma unroll
-      for (int off = RL / 2; off >= 1; off >>= 1)
+      for (int off = SL / 2; off >= 1; off >>= 1)
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) part[hh] += __shfl_xor(part[hh], off);
-      if (valid && sub == 0) {
+      if (valid && ssub == 0) {
         float S = 0.0f;
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
