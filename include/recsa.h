@@ -102,15 +102,15 @@ int32_t recsa_sel_width(const recsa_shape_t* shape, int64_t n_min, int64_t n_max
                         const int32_t* k_per_level /*[host] n_levels*/, int32_t n_levels);
 
 /* Workspace bytes needed by recsa_decode / recsa_prefill for visible prefixes of up to
- * n_max tokens, or by recsa_dense_ref_attn (k_per_level = NULL) for positions up to n_max.
- * -1 if invalid. */
+ * n_max tokens (the RoPE table for candidate positions). -1 if invalid. */
 int64_t recsa_workspace_bytes(const recsa_shape_t* shape, int64_t n_max,
-                              const int32_t* k_per_level /*[host] or NULL*/, int32_t n_levels);
+                              const int32_t* k_per_level /*[host]*/, int32_t n_levels);
 
 /* Step 1, tree build [Abstract, Core Idea].
  * Builds every node that is complete at n_new tokens but not at n_old, bottom level first:
  *   m = (sum of the f children's stored keys, in child order, float32) / f
- *   NK = round(W @ m)      (each output accumulated input by input, float32, no fused multiply-add)
+ *   NK = round(W @ m)      (each output accumulated input by input in float32, one fused
+ *                           multiply-add -- a single rounding -- per term)
  *   NV = round((sum of the f children's stored values, in child order, float32) / f)
  * Children are token rows at level 1 and stored level-(l-1) nodes above. Nodes complete at
  * n_old are left untouched, so growing the cache in any number of steps gives the same tree.
@@ -156,15 +156,27 @@ int32_t recsa_prefill(const recsa_shape_t* shape, const void* q, int64_t q_start
 
 /* Dense softmax attention with standard RoPE at the original positions -- the comparator the
  * method is timed against [Abstract]; also RecSA's limit when every level keeps everything.
- *   causal = 0: decode, every query at position n_tokens against keys 0..n_tokens-1
- *   (q_start ignored). causal = 1: query j at position t = q_start + j against keys 0..t
- *   (q_start + n_q <= n_tokens).
- *   q [dev]: [B][n_q][H_q][d]; out float32 [B][n_q][H_q][d]; lse float32 [B][n_q][H_q] (nullable).
- *   workspace: recsa_workspace_bytes(shape, n_tokens, NULL, 0).
+ * mode: RECSA_DENSE_CAUSAL (bit 0) and/or RECSA_DENSE_KEYS_ROTATED (bit 1).
+ *   not causal: decode, every query at position n_tokens against keys 0..n_tokens-1 (q_start ignored).
+ *   causal: query j at position t = q_start + j against keys 0..t (q_start + n_q <= n_tokens).
+ *   keys rotated: K already holds each key rotated at its own position (recsa_rotate_keys), as a
+ *   dense cache usually stores it; otherwise K is pre-RoPE and is rotated into the workspace first.
+ *   q [dev]: [B][n_q][H_q][d] pre-RoPE; out float32 [B][n_q][H_q][d]; lse float32 [B][n_q][H_q] (nullable).
+ *   bf16 runs on the matrix cores with the probabilities rounded to bf16 for P V; float32 runs on
+ *   the vector units. workspace: recsa_dense_workspace_bytes(shape, n_tokens, n_q, mode).
  * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED, WORKSPACE. */
+#define RECSA_DENSE_CAUSAL 1
+#define RECSA_DENSE_KEYS_ROTATED 2
+int64_t recsa_dense_workspace_bytes(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q, int32_t mode);
 int32_t recsa_dense_ref_attn(const recsa_shape_t* shape, const void* q, int64_t q_start, int64_t n_q,
-                             const void* K, const void* V, int64_t n_tokens, int32_t causal,
+                             const void* K, const void* V, int64_t n_tokens, int32_t mode,
                              float* out, float* lse, void* workspace, int64_t ws_bytes, void* stream);
+
+/* Rotates the first n_tokens keys of every slice at their own positions (standard RoPE, the
+ * same rounding as the tree path): K_rot[b][h][p] = round(rot(K[b][h][p], p)).
+ *   K, K_rot [dev]: [B][H_kv][capacity][d]; they must not overlap.
+ * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED. */
+int32_t recsa_rotate_keys(const recsa_shape_t* shape, const void* K, int64_t n_tokens, void* K_rot, void* stream);
 
 #ifdef __cplusplus
 }

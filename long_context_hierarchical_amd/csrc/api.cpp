@@ -286,7 +286,6 @@ int64_t recsa_workspace_bytes(const recsa_shape_t* shape, int64_t n_max, const i
     fail(RECSA_ERR_INVALID_ARG, "n_max must be >= 0");
     return -1;
   }
-  if (!k) return table_bytes(I, n_max);  // dense: positions 0..n_max
   if (check_k(k, n_levels, levels_of(n_max, I.f))) return -1;
   return table_bytes(I, bounds_for(I, n_max, k).P);
 }
@@ -356,15 +355,134 @@ int32_t recsa_prefill(const recsa_shape_t* shape, const void* q, int64_t q_start
                     ws_bytes, stream);
 }
 
-int32_t recsa_dense_ref_attn(const recsa_shape_t* shape, const void* q, int64_t q_start, int64_t n_q, const void* K,
-                             const void* V, int64_t n_tokens, int32_t causal, float* out, float* lse, void* workspace,
-                             int64_t ws_bytes, void* stream) {
-  (void)q; (void)q_start; (void)n_q; (void)K; (void)V; (void)n_tokens; (void)causal; (void)out; (void)lse;
-  (void)workspace; (void)ws_bytes; (void)stream;
+struct DensePlan {
+  int64_t kr_bytes = 0, part_o_bytes = 0, part_ml_bytes = 0, total = 0, keys_per_split = 0;
+  int32_t splits = 1;
+};
+
+static DensePlan dense_plan(const Info& I, int64_t n_tokens, int64_t n_q, int32_t mode) {
+  DensePlan p;
+  const bool causal = mode & RECSA_DENSE_CAUSAL;
+  const bool rotated = mode & RECSA_DENSE_KEYS_ROTATED;
+  if (!rotated && I.theta != 0.0f) p.kr_bytes = ((I.B * I.Hkv * n_tokens * I.d * I.esz) + 255) / 256 * 256;
+  p.keys_per_split = std::max<int64_t>(n_tokens, 1);
+  if (I.bf16 && !causal && n_tokens > 0 && n_q > 0) {
+    const int64_t qpb = recsa::dense_queries_per_block(static_cast<int>(I.G));
+    const int64_t wgs = (n_q + qpb - 1) / qpb * I.B * I.Hkv;
+    int64_t splits = std::max<int64_t>(1, (2048 + wgs - 1) / wgs);
+    splits = std::min<int64_t>(splits, (n_tokens + 255) / 256);
+    int64_t kps = (n_tokens + splits - 1) / splits;
+    kps = (kps + 63) / 64 * 64;
+    splits = (n_tokens + kps - 1) / kps;
+    p.splits = static_cast<int32_t>(splits);
+    p.keys_per_split = kps;
+  }
+  if (p.splits > 1) {
+    const int64_t rows = p.splits * I.B * I.Hkv * n_q * I.G;
+    p.part_o_bytes = (rows * I.d * 4 + 255) / 256 * 256;
+    p.part_ml_bytes = (rows * 2 * 4 + 255) / 256 * 256;
+  }
+  p.total = p.kr_bytes + p.part_o_bytes + p.part_ml_bytes;
+  return p;
+}
+
+static recsa::InvFreq inv_freq_of(const Info& I) {
+  recsa::InvFreq iv{};
+  for (int i = 0; i < I.d / 2; ++i)
+    iv.w[i] = static_cast<float>(std::pow(static_cast<double>(I.theta), -2.0 * i / static_cast<double>(I.d)));
+  return iv;
+}
+
+int64_t recsa_dense_workspace_bytes(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q, int32_t mode) {
+  Info I;
+  if (check_shape(shape, &I)) return -1;
+  if (n_tokens < 0 || n_q < 0 || (mode & ~3)) {
+    fail(RECSA_ERR_INVALID_ARG, "need n_tokens >= 0, n_q >= 0 and mode in 0..3");
+    return -1;
+  }
+  return dense_plan(I, n_tokens, n_q, mode).total;
+}
+
+int32_t recsa_rotate_keys(const recsa_shape_t* shape, const void* K, int64_t n_tokens, void* K_rot, void* stream) {
   Info I;
   int32_t rc = check_shape(shape, &I);
   if (rc) return rc;
-  return fail(RECSA_ERR_UNSUPPORTED, "dense reference attention is not built yet");
+  if (n_tokens < 0) return fail(RECSA_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (n_tokens > I.cap) return fail(RECSA_ERR_CAPACITY, "n_tokens %lld exceeds the capacity %lld", (long long)n_tokens,
+                                    (long long)I.cap);
+  if (n_tokens == 0) return RECSA_OK;
+  if (!K || !K_rot) return fail(RECSA_ERR_INVALID_ARG, "K or K_rot is NULL");
+  if (!aligned16(K) || !aligned16(K_rot)) return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const int64_t bytes = I.B * I.Hkv * I.cap * I.d * I.esz;
+  const char* a = static_cast<const char*>(K);
+  const char* b = static_cast<const char*>(K_rot);
+  if (a < b + bytes && b < a + bytes) return fail(RECSA_ERR_INVALID_ARG, "K and K_rot overlap");
+  hipError_t e = recsa::launch_rotate_keys(K, I.cap, K_rot, I.cap, n_tokens, I.B * I.Hkv, static_cast<int>(I.d), I.bf16,
+                                           inv_freq_of(I), I.theta != 0.0f, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "key rotation launch");
+  return RECSA_OK;
+}
+
+int32_t recsa_dense_ref_attn(const recsa_shape_t* shape, const void* q, int64_t q_start, int64_t n_q, const void* K,
+                             const void* V, int64_t n_tokens, int32_t mode, float* out, float* lse, void* workspace,
+                             int64_t ws_bytes, void* stream) {
+  Info I;
+  int32_t rc = check_shape(shape, &I);
+  if (rc) return rc;
+  if (mode & ~3) return fail(RECSA_ERR_INVALID_ARG, "mode must be in 0..3");
+  const bool causal = mode & RECSA_DENSE_CAUSAL;
+  const bool rotated = mode & RECSA_DENSE_KEYS_ROTATED;
+  if (n_q < 0 || n_tokens < 0) return fail(RECSA_ERR_INVALID_ARG, "n_q and n_tokens must be >= 0");
+  if (causal && (q_start < 0 || q_start + n_q > n_tokens))
+    return fail(RECSA_ERR_INVALID_ARG, "causal queries need 0 <= q_start and q_start + n_q <= n_tokens");
+  if (n_tokens > I.cap) return fail(RECSA_ERR_CAPACITY, "n_tokens %lld exceeds the capacity %lld", (long long)n_tokens,
+                                    (long long)I.cap);
+  if (n_q * I.Hkv > INT32_MAX || I.B * I.Hkv > 65535) return fail(RECSA_ERR_UNSUPPORTED, "grid too large");
+  if (n_q == 0) return RECSA_OK;
+  if (!q || !out || (n_tokens > 0 && (!K || !V))) return fail(RECSA_ERR_INVALID_ARG, "q, K, V or out is NULL");
+  if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(workspace))
+    return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const DensePlan pl = dense_plan(I, n_tokens, n_q, mode);
+  if (ws_bytes < pl.total) return fail(RECSA_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes,
+                                       (long long)pl.total);
+  if (pl.total > 0 && !workspace) return fail(RECSA_ERR_INVALID_ARG, "workspace is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const recsa::InvFreq iv = inv_freq_of(I);
+  recsa::DenseArgs a{};
+  a.q = q;
+  a.V = V;
+  a.out = out;
+  a.lse = lse;
+  a.v_rows = I.cap;
+  a.n_q = n_q;
+  a.q_start = causal ? q_start : 0;
+  a.n_tokens = n_tokens;
+  a.causal = causal ? 1 : 0;
+  a.Hkv = static_cast<int32_t>(I.Hkv);
+  a.Hq = static_cast<int32_t>(I.Hq);
+  a.scale = I.scale;
+  a.use_rope = I.theta != 0.0f;
+  a.iv = iv;
+  a.n_splits = pl.splits;
+  a.keys_per_split = pl.keys_per_split;
+  char* ws = static_cast<char*>(workspace);
+  if (rotated || I.theta == 0.0f) {
+    a.Kr = K;
+    a.kr_rows = I.cap;
+  } else {
+    hipError_t e = recsa::launch_rotate_keys(K, I.cap, ws, n_tokens, n_tokens, I.B * I.Hkv, static_cast<int>(I.d),
+                                             I.bf16, iv, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "key rotation launch");
+    a.Kr = ws;
+    a.kr_rows = n_tokens;
+  }
+  if (pl.splits > 1) {
+    a.part_o = reinterpret_cast<float*>(ws + pl.kr_bytes);
+    a.part_ml = reinterpret_cast<float*>(ws + pl.kr_bytes + pl.part_o_bytes);
+  }
+  hipError_t e = recsa::launch_dense(a, static_cast<int>(I.d), I.bf16, static_cast<int>(I.G), I.B, st);
+  if (e != hipSuccess) return hip_fail(e, "dense attention launch");
+  return RECSA_OK;
 }
 
 }  // extern "C"

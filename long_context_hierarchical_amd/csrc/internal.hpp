@@ -75,6 +75,34 @@ struct AttnArgs {
 };
 
 size_t attend_lds_bytes(int d, int G, int smax, int zcap);
+
+// ---------------------------------------------------------------- dense reference attention
+// Keys rotated at their own positions: Kr[bh][p] = round(rot(K[bh][p], p)), p < n
+// (K rows per slice: cap; Kr rows per slice: kr_rows).
+hipError_t launch_rotate_keys(const void* K, int64_t cap, void* Kr, int64_t kr_rows, int64_t n, int64_t BH, int d,
+                              bool bf16, const InvFreq& iv, int use_rope, hipStream_t s);
+
+struct DenseArgs {
+  const void* q;        // [B][n_q][H_q][d]
+  const void* Kr;       // rotated keys [B*H_kv][kr_rows][d]
+  const void* V;        // [B*H_kv][v_rows][d]
+  float* out;           // [B][n_q][H_q][d]
+  float* lse;           // [B][n_q][H_q] or null
+  float* part_o;        // split partials [splits][B*H_kv][n_q*G][d] (null when one split)
+  float* part_ml;       // [splits][B*H_kv][n_q*G][2]
+  int64_t kr_rows, v_rows;
+  int64_t n_q, q_start, n_tokens;
+  int32_t causal;
+  int32_t Hkv, Hq;
+  int64_t keys_per_split;
+  int32_t n_splits;
+  float scale;
+  int32_t use_rope;
+  InvFreq iv;
+};
+// Query rows per workgroup of the dense kernel (G query heads of one KV head per query).
+int dense_queries_per_block(int G);
+hipError_t launch_dense(const DenseArgs& a, int d, bool bf16, int G, int64_t B, hipStream_t s);
 hipError_t launch_attend(const AttnArgs& a, int d, bool bf16, int G, size_t lds, int64_t B, hipStream_t s);
 
 }  // namespace recsa

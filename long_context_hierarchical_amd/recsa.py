@@ -21,8 +21,9 @@ INT32_MAX = 2 ** 31 - 1
 EXPORTS = (
     "recsa_abi_version", "recsa_last_error", "recsa_num_levels", "recsa_tree_bytes", "recsa_level_offset",
     "recsa_sel_width", "recsa_workspace_bytes", "recsa_build_tree", "recsa_decode", "recsa_prefill",
-    "recsa_dense_ref_attn",
+    "recsa_dense_workspace_bytes", "recsa_dense_ref_attn", "recsa_rotate_keys",
 )
+RECSA_DENSE_CAUSAL, RECSA_DENSE_KEYS_ROTATED = 1, 2
 
 
 class RecsaError(RuntimeError):
@@ -84,7 +85,9 @@ def lib() -> ctypes.CDLL:
             "recsa_build_tree": (I32, [SP, P, P, P, I64, I64, P, P]),
             "recsa_decode": (I32, [SP, P, I64, P, P, P, I64, K, I32, P, P, P, I32, P, I64, P]),
             "recsa_prefill": (I32, [SP, P, I64, I64, P, P, P, K, I32, P, P, P, I32, P, I64, P]),
+            "recsa_dense_workspace_bytes": (I64, [SP, I64, I64, I32]),
             "recsa_dense_ref_attn": (I32, [SP, P, I64, I64, P, P, I64, I32, P, P, P, I64, P]),
+            "recsa_rotate_keys": (I32, [SP, P, I64, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -142,11 +145,13 @@ def recsa_sel_width(shape: Shape, n_min: int, n_max: int, k_levels) -> int:
     return _nbytes(lib().recsa_sel_width(ctypes.byref(shape.c()), n_min, n_max, k, nl))
 
 
-def recsa_workspace_bytes(shape: Shape, n_max: int, k_levels=None) -> int:
-    if k_levels is None:
-        return _nbytes(lib().recsa_workspace_bytes(ctypes.byref(shape.c()), n_max, None, 0))
+def recsa_workspace_bytes(shape: Shape, n_max: int, k_levels) -> int:
     k, nl = _k(k_levels)
     return _nbytes(lib().recsa_workspace_bytes(ctypes.byref(shape.c()), n_max, k, nl))
+
+
+def recsa_dense_workspace_bytes(shape: Shape, n_tokens: int, n_q: int, mode: int) -> int:
+    return _nbytes(lib().recsa_dense_workspace_bytes(ctypes.byref(shape.c()), n_tokens, n_q, mode))
 
 
 # ----------------------------------------------------------------- entry points
@@ -174,13 +179,16 @@ def recsa_prefill(shape: Shape, q, q_start: int, K, V, tree, k_levels, out, lse=
                                _p(out), _p(lse), _p(sel), sel_width, _p(workspace), ws_bytes, _stream(stream)))
 
 
-def recsa_dense_ref_attn(shape: Shape, q, q_start: int, K, V, n_tokens: int, causal: bool, out, lse=None,
+def recsa_dense_ref_attn(shape: Shape, q, q_start: int, K, V, n_tokens: int, mode: int, out, lse=None,
                          workspace=None, stream=None):
     n_q = q.shape[1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().recsa_dense_ref_attn(ctypes.byref(shape.c()), _p(q), q_start, n_q, _p(K), _p(V), n_tokens,
-                                      1 if causal else 0, _p(out), _p(lse), _p(workspace), ws_bytes,
-                                      _stream(stream)))
+                                      mode, _p(out), _p(lse), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def recsa_rotate_keys(shape: Shape, K, n_tokens: int, K_rot, stream=None):
+    _check(lib().recsa_rotate_keys(ctypes.byref(shape.c()), _p(K), n_tokens, _p(K_rot), _stream(stream)))
 
 
 # ----------------------------------------------------------------- views

@@ -18,6 +18,7 @@ from .recsa import (  # noqa: F401
     level_counts,
     plan_counts,
     prefill,
+    rope_rows,
     rope_table,
     rotate,
     round_store,
