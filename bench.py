@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=24, help="oracle decode units timed for the baseline")
     ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--step-mode", action="store_true", help="also time one-query-per-sequence decode calls")
+    ap.add_argument("--no-legs", action="store_true", help="skip the dense and prefill comparison legs")
+    ap.add_argument("--prefill-chunk", type=int, default=4096)
     return ap.parse_args()
 
 
@@ -249,6 +251,63 @@ def main():
             "roofline_other": roof("attend_kernel" if dom == "pool_level_kernel" else "pool_level_kernel"),
         },
     }
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    if not args.no_legs:
+        log("comparison legs: dense decode, prefill")
+        legs = {}
+        # dense attention at the same context; keys rotated once beforehand, as a dense cache holds them
+        Kr = torch.empty_like(K)
+        R.recsa_rotate_keys(sh, K, w.L, Kr)
+        mode = R.RECSA_DENSE_KEYS_ROTATED
+        dws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, w.n_queries, mode), 16), dtype=torch.uint8,
+                          device=dev)
+        dout = torch.empty_like(out)
+        ms = timed(lambda: R.recsa_dense_ref_attn(sh, q, 0, Kr, V, w.L, mode, dout, None, dws), 3)
+        legs["dense_decode_batched"] = {"ms_per_call": round(ms, 4), "queries_per_call": n_queries,
+                                        "queries_per_s": round(n_queries / (ms * 1e-3), 1)}
+        q1 = q[:, :1].contiguous()
+        o1 = torch.empty(w.B, 1, w.Hq, w.d, dtype=torch.float32, device=dev)
+        dws1 = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, 1, mode), 16), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: R.recsa_dense_ref_attn(sh, q1, 0, Kr, V, w.L, mode, o1, None, dws1), 10)
+        legs["dense_decode_step"] = {"ms_per_call": round(ms, 4), "queries_per_call": w.B,
+                                     "queries_per_s": round(w.B / (ms * 1e-3), 1),
+                                     "GBps": round(2 * w.B * w.Hkv * w.L * w.d * w.elem_bytes / (ms * 1e-3) / 1e9, 1)}
+        # causal prefill of the last chunk of positions [L - c, L): RecSA over the built tree, dense over all keys
+        from synthetic import with_overrides
+        c = args.prefill_chunk
+        wq = with_overrides(w, seed=w.seed + 1000)
+        qp = torch.empty(w.B, c, w.Hq, w.d, dtype=td, device=dev)
+        for b in range(w.B):
+            qp[b] = up(gen_queries(wq, b, c))
+        pout = torch.empty(w.B, c, w.Hq, w.d, dtype=torch.float32, device=dev)
+        pws = torch.empty(R.recsa_workspace_bytes(sh, w.L, k), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: R.recsa_prefill(sh, qp, w.L - c, K, V, tree, k, pout, None, None, 0, pws), 3)
+        legs["recsa_prefill_last_chunk"] = {"ms_per_call": round(ms, 4), "tokens_per_call": w.B * c,
+                                            "tokens_per_s": round(w.B * c / (ms * 1e-3), 1),
+                                            "positions": [w.L - c, w.L]}
+        pmode = R.RECSA_DENSE_KEYS_ROTATED | R.RECSA_DENSE_CAUSAL
+        dpws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, c, pmode), 16), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: R.recsa_dense_ref_attn(sh, qp, w.L - c, Kr, V, w.L, pmode, pout, None, dpws), 2)
+        flops = 4.0 * w.B * w.Hq * w.d * sum(range(w.L - c + 1, w.L + 1))
+        legs["dense_prefill_last_chunk"] = {"ms_per_call": round(ms, 4), "tokens_per_call": w.B * c,
+                                            "tokens_per_s": round(w.B * c / (ms * 1e-3), 1),
+                                            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1)}
+        legs["speedup_decode_batched"] = round(legs["dense_decode_batched"]["ms_per_call"] / decode_ms, 2)
+        legs["speedup_prefill_last_chunk"] = round(legs["dense_prefill_last_chunk"]["ms_per_call"] /
+                                                   legs["recsa_prefill_last_chunk"]["ms_per_call"], 2)
+        del Kr
+        res["breakdown"]["legs"] = legs
 
     if args.step_mode:
         one_q = q[:, :1].contiguous()
