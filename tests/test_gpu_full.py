@@ -31,6 +31,7 @@ def _upload_workload(w, n_q):
             Kb, Vb = gen_kv_slice(w, b, h, qb)
             K[b, h] = torch.from_numpy(Kb).view(td).to(dev)
             V[b, h] = torch.from_numpy(Vb).view(td).to(dev)
+            _say(f"  {w.name}: slice ({b}, {h}) uploaded")
     q = np.stack(qs)
     qd = torch.from_numpy(q).view(td).to(dev)
     W = gen_W(w)
