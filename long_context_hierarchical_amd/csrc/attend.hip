@@ -16,8 +16,10 @@
 //               storage type; the query heads rotated at C and rounded; the
 //               logit z = scale * <q~, k~> per head (float32, any order), the
 //               group score S = sum over the G heads of the KV group.
-//   select      the s = min(k, C) largest (S, -i) keys: s rounds of a wave-wide
-//               64-bit max (exact, deterministic, lowest index wins ties).
+//   select      the s = min(k, C) largest (S, -i) keys: the s-th largest score by
+//               bisection on its order-preserving bits (ballot counts), then the
+//               scores above it and, lowest index first, those equal to it
+//               (exact, deterministic).
 //   softmax     unkept candidates join the online softmax with their node's
 //               mean value; kept ones become the next level's parents.
 // Token level: the tokens under the kept level-1 nodes plus the trailing
@@ -30,9 +32,14 @@
 // elements [8s, 8s+8) and their rotate-half partners [D/2 + 8s, ...), so the
 // rotation needs no lane exchange and the per-row reduction is 3 (d=128)
 // shuffle steps; bf16 operands are rounded and packed by v_cvt_pk_bf16_f32 and
-// dotted by v_dot2 (the G query heads share each loaded row). In the value
-// phase D/8 lanes per row, a lane holding elements [8s, 8s+8).
+// dotted by v_dot2 (the G query heads share each loaded row); the rotated query
+// operands sit in LDS, and the rows of the next pass are loaded before the
+// current pass is computed. In the value phase D/4 lanes per row, a lane
+// holding elements [4s, 4s+4), 8 rows per pass. The kernel is held
+// to 128 VGPRs (4 waves per SIMD) for groups of up to 4 query heads.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -53,12 +60,6 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(v)), m));
-  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(static_cast<uint32_t>(v >> 32)), m));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
 // 4 consecutive storage elements -> float.
 template <bool BF16>
 __device__ __forceinline__ void load4(const void* base, int64_t off, float (&x)[4]) {
@@ -75,7 +76,7 @@ __device__ __forceinline__ void load4(const void* base, int64_t off, float (&x)[
 }
 
 struct Lds {
-  uint32_t q, zs, sc, flags, selA, selB, nls, total;
+  uint32_t q, qr, zs, sc, flags, selA, selB, nls, total;
 };
 
 __host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
@@ -84,6 +85,7 @@ __host__ __device__ inline Lds lds_layout(int d, int G, int smax, int zcap) {
   Lds L;
   uint32_t o = 0;
   L.q = o;     o = align16(o + 4u * G * d);         // raw query heads of the KV group
+  L.qr = o;    o = align16(o + 4u * G * d);         // rotated query operands of the current level
   L.zs = o;    o = align16(o + 4u * G * zcap);      // logits, then softmax weights, [G][zcap]
   L.sc = o;    o = align16(o + 4u * zcap);          // group scores
   L.flags = o; o = align16(o + zcap);               // kept flags
@@ -99,29 +101,135 @@ size_t attend_lds_bytes(int d, int G, int smax, int zcap) {
 }
 
 // Candidate index -> node (or token) id: children of the kept parents, then orphans.
+// Ids and indices fit in 32 bits (the capacity is at most INT32_MAX); a power-of-two
+// fanout splits an index with a shift and a mask.
 struct CandMap {
   const int32_t* parents;
-  int64_t n_kids;   // f * (number of kept parents)
-  int64_t orph;     // first orphan id
-  int f;
-  __device__ __forceinline__ int64_t operator()(int64_t i) const {
-    return i < n_kids ? static_cast<int64_t>(f) * parents[i / f] + i % f : orph + (i - n_kids);
+  int32_t n_kids;   // f * (number of kept parents)
+  int32_t orph;     // first orphan id
+  int32_t f;
+  int32_t fshift;   // log2(f) when f is a power of two, else -1
+  __device__ __forceinline__ int32_t operator()(int32_t i) const {
+    if (i >= n_kids) return orph + (i - n_kids);
+    int32_t p, c;
+    if (fshift >= 0) {
+      p = i >> fshift;
+      c = i & (f - 1);
+    } else {
+      p = i / f;
+      c = i - p * f;
+    }
+    return f * parents[p] + c;
   }
 };
 
+// One row fragment of 8 storage elements, as loaded (converted later).
+template <bool BF16>
+struct Raw8 {
+  uint4 u[BF16 ? 1 : 2];
+};
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> raw8_load(const void* base, int64_t off) {
+  Raw8<BF16> r;
+  if constexpr (BF16) {
+    r.u[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + off);
+    r.u[0] = p[0];
+    r.u[1] = p[1];
+  }
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> raw8_zero() {
+  Raw8<BF16> r;
+#pragma unroll
+  for (int i = 0; i < (BF16 ? 1 : 2); ++i) r.u[i] = make_uint4(0u, 0u, 0u, 0u);
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void raw8_cvt(const Raw8<BF16>& r, float (&x)[8]) {
+  if constexpr (BF16) {
+    const uint32_t w[4] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      x[4 * k] = __uint_as_float(r.u[k].x);
+      x[4 * k + 1] = __uint_as_float(r.u[k].y);
+      x[4 * k + 2] = __uint_as_float(r.u[k].z);
+      x[4 * k + 3] = __uint_as_float(r.u[k].w);
+    }
+  }
+}
+
+// One row fragment of 4 storage elements, as loaded (converted later).
+template <bool BF16>
+struct Raw4 {
+  typename std::conditional<BF16, uint2, uint4>::type u;
+};
+
+template <bool BF16>
+__device__ __forceinline__ Raw4<BF16> raw4_load(const void* base, int64_t off) {
+  Raw4<BF16> r;
+  if constexpr (BF16) {
+    r.u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
+  } else {
+    r.u = *reinterpret_cast<const uint4*>(static_cast<const float*>(base) + off);
+  }
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ Raw4<BF16> raw4_zero() {
+  Raw4<BF16> r;
+  if constexpr (BF16) {
+    r.u = make_uint2(0u, 0u);
+  } else {
+    r.u = make_uint4(0u, 0u, 0u, 0u);
+  }
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void raw4_cvt(const Raw4<BF16>& r, float (&x)[4]) {
+  if constexpr (BF16) {
+    x[0] = __uint_as_float(r.u.x << 16);
+    x[1] = __uint_as_float(r.u.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(r.u.y << 16);
+    x[3] = __uint_as_float(r.u.y & 0xFFFF0000u);
+  } else {
+    x[0] = __uint_as_float(r.u.x);
+    x[1] = __uint_as_float(r.u.y);
+    x[2] = __uint_as_float(r.u.z);
+    x[3] = __uint_as_float(r.u.w);
+  }
+}
+
 template <int D, bool BF16, int G>
-__global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
-  constexpr int RL = D / 8;            // lanes per row, value phase (8 elements per lane)
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void attend_kernel(AttnArgs a) {
+  constexpr int VE = 4;                // elements per lane, value phase
+  constexpr int RL = D / VE;           // lanes per row, value phase
   constexpr int RPP = kWave / RL;      // rows per pass, value phase
   constexpr int SL = D / 16;           // lanes per row, score phase (8 rotate-half pairs per lane)
   constexpr int SPP = kWave / SL;      // rows per pass, score phase
   constexpr int HALF = D / 2;
-  constexpr int PV_UNROLL = 2;
+  constexpr int PV_UNROLL = 4;
 
   extern __shared__ __align__(16) unsigned char lds[];
   const int zcap = a.zcap;
   const Lds L = lds_layout(D, G, a.smax, zcap);
   float* qs = reinterpret_cast<float*>(lds + L.q);
+  // rotated query operands, [G][D/16 lane slots][16 words]: bf16 packs 8 pairs
+  // (lo0,lo1), (lo2,lo3), .., (hi6,hi7) into words 0..7; float32 keeps lo0..lo7, hi0..hi7
+  uint32_t* qr = reinterpret_cast<uint32_t*>(lds + L.qr);
   float* zs = reinterpret_cast<float*>(lds + L.zs);
   float* sc = reinterpret_cast<float*>(lds + L.sc);
   uint8_t* flags = reinterpret_cast<uint8_t*>(lds + L.flags);
@@ -167,19 +275,17 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
       for (int c = lane; c < a.sel_width; c += kWave) a.sel[(sel_row0 + lv - 1) * a.sel_width + c] = -1;
   }
 
-  float m_run[G], l_run[G], acc[G][8];
+  float m_run[G], l_run[G], acc[G][VE];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     m_run[hh] = -INFINITY;
     l_run[hh] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.0f;
+    for (int e = 0; e < VE; ++e) acc[hh][e] = 0.0f;
   }
 
-  // rotated query operands for the current level: this lane's 8 rotate-half pairs
-  // (elements 8*ssub + e and HALF + 8*ssub + e, e < 8) of every head
-  bf16x2_t qp[G][8];   // bf16: packed (lo0,lo1), (lo2,lo3), .., (hi6,hi7)
-  float qf[G][16];     // f32: lo0..lo7, hi0..hi7
+  // rotated query operands for the current level -> qr: lane slot ssub holds the 8
+  // rotate-half pairs (elements 8*ssub + e and HALF + 8*ssub + e, e < 8) of every head
   auto rotate_query = [&](int64_t pos) {
     float c[8], s[8];
     if (a.use_rope) {
@@ -213,40 +319,55 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
           hi[e] = qh[e];
         }
       }
-      if constexpr (BF16) {
+      uint32_t* dst = qr + (hh * SL + ssub) * 16;
+      if (srg == 0) {
+        if constexpr (BF16) {
+          uint32_t w[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          qp[hh][u] = pack_bf16_rne(lo[2 * u], lo[2 * u + 1]);
-          qp[hh][4 + u] = pack_bf16_rne(hi[2 * u], hi[2 * u + 1]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qf[hh][e] = lo[e];
-          qf[hh][8 + e] = hi[e];
+          for (int u = 0; u < 4; ++u) {
+            w[u] = __builtin_bit_cast(uint32_t, pack_bf16_rne(lo[2 * u], lo[2 * u + 1]));
+            w[4 + u] = __builtin_bit_cast(uint32_t, pack_bf16_rne(hi[2 * u], hi[2 * u + 1]));
+          }
+          reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+          reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        } else {
+          reinterpret_cast<float4*>(dst)[0] = make_float4(lo[0], lo[1], lo[2], lo[3]);
+          reinterpret_cast<float4*>(dst)[1] = make_float4(lo[4], lo[5], lo[6], lo[7]);
+          reinterpret_cast<float4*>(dst)[2] = make_float4(hi[0], hi[1], hi[2], hi[3]);
+          reinterpret_cast<float4*>(dst)[3] = make_float4(hi[4], hi[5], hi[6], hi[7]);
         }
       }
     }
+    wave_sync();
   };
 
   // logits of candidates [c0, c0 + cn) (index = RoPE position) -> zs[hh * zcap + r], sc[r]
-  auto score_rows = [&](const void* src, int64_t rowbase, const CandMap& cm, int64_t c0, int64_t cn) {
-    for (int64_t r0 = 0; r0 < cn; r0 += SPP) {
-      const int64_t r = r0 + srg;
-      const bool valid = r < cn;
-      const int64_t i = c0 + r;
-      float klo[8], khi[8];
-      if (valid) {
-        const int64_t off = (rowbase + cm(i)) * D + 8 * ssub;
-        load8<BF16>(src, off, klo);
-        load8<BF16>(src, off + HALF, khi);
+  // The rows of the next pass are loaded before the current pass is computed.
+  auto score_rows = [&](const void* src, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn) {
+    auto fetch = [&](int32_t r0, Raw8<BF16>& lo, Raw8<BF16>& hi) {
+      const int32_t r = r0 + srg;
+      if (r < cn) {
+        const int64_t off = (rowbase + cm(c0 + r)) * D + 8 * ssub;
+        lo = raw8_load<BF16>(src, off);
+        hi = raw8_load<BF16>(src, off + HALF);
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { klo[e] = 0.0f; khi[e] = 0.0f; }
+        lo = raw8_zero<BF16>();
+        hi = raw8_zero<BF16>();
       }
+    };
+    Raw8<BF16> nlo, nhi;
+    fetch(0, nlo, nhi);
+    for (int32_t r0 = 0; r0 < cn; r0 += SPP) {
+      const int32_t r = r0 + srg;
+      const bool valid = r < cn;
+      const int32_t i = c0 + r;
+      float klo[8], khi[8];
+      raw8_cvt<BF16>(nlo, klo);
+      raw8_cvt<BF16>(nhi, khi);
+      if (r0 + SPP < cn) fetch(r0 + SPP, nlo, nhi);
       float olo[8], ohi[8];
       if (a.use_rope) {
-        const float4* t = reinterpret_cast<const float4*>(a.tab + (valid ? i : 0) * HALF + 8 * ssub);
+        const float4* t = reinterpret_cast<const float4*>(a.tab + static_cast<int64_t>(valid ? i : 0) * HALF + 8 * ssub);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float4 tv = t[u];
@@ -274,19 +395,24 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
+          const uint4* src4 = reinterpret_cast<const uint4*>(qr + (hh * SL + ssub) * 16);
+          const uint4 qa = src4[0], qb = src4[1];
+          const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
           float p = 0.0f;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) p = __builtin_amdgcn_fdot2_f32_bf16(kp[u], qp[hh][u], p, false);
+          for (int u = 0; u < 8; ++u)
+            p = __builtin_amdgcn_fdot2_f32_bf16(kp[u], __builtin_bit_cast(bf16x2_t, qw[u]), p, false);
           part[hh] = p;
         }
       } else {
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
+          const float* qf = reinterpret_cast<const float*>(qr + (hh * SL + ssub) * 16);
           float p = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) p = fmaf(qf[hh][e], olo[e], p);
+          for (int e = 0; e < 8; ++e) p = fmaf(qf[e], olo[e], p);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) p = fmaf(qf[hh][8 + e], ohi[e], p);
+          for (int e = 0; e < 8; ++e) p = fmaf(qf[8 + e], ohi[e], p);
           part[hh] = p;
         }
       }
@@ -308,44 +434,67 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
     wave_sync();
   };
 
-  // flags[r] = 1 for the s largest (S, -r) keys among r < C
-  auto select_top = [&](int64_t C, int64_t s) {
-    for (int64_t r = lane; r < C; r += kWave) flags[r] = 0;
-    wave_sync();
-    uint64_t best = 0;
-    int64_t slot = -1;
-    for (int64_t r = lane; r < C; r += kWave) {
-      const uint64_t k = select_key(sc[r], static_cast<uint32_t>(r));
-      if (k > best) { best = k; slot = r; }
-    }
-    for (int64_t it = 0; it < s; ++it) {
-      uint64_t w = best;
+  // Keeps the s largest (S, -r) keys among r < C: flags[r] = 1 and sel_out[0..s) = their
+  // node ids in candidate order. The s-th largest score is found by bisection on its
+  // order-preserving 32-bit pattern (a ballot count per step, no lane exchange); the
+  // candidates above it are kept, then those equal to it in index order.
+  auto select_top = [&](int32_t C, int32_t s, const CandMap& cm, int32_t* sel_out) {
+    const int32_t nu = (C + kWave - 1) / kWave;
+    uint32_t o[4];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const uint64_t o = shfl_xor_u64(w, off);
-        w = o > w ? o : w;
-      }
-      if (best == w) {            // keys are unique: exactly one lane holds the maximum
-        flags[slot] = 1;
-        best = 0;
-        slot = -1;
-        for (int64_t r = lane; r < C; r += kWave) {
-          if (flags[r]) continue;
-          const uint64_t k = select_key(sc[r], static_cast<uint32_t>(r));
-          if (k > best) { best = k; slot = r; }
-        }
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int32_t r = lane + kWave * u;
+      o[u] = r < C ? ordered_bits(sc[r]) : 0u;
     }
+    auto key = [&](int u) -> uint32_t {
+      const int32_t r = lane + kWave * u;
+      return r < C ? ordered_bits(sc[r]) : 0u;
+    };
+    // candidates with key >= t (t > 0; an empty slot holds 0)
+    auto count_ge = [&](uint32_t t) -> int32_t {
+      int32_t c = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) c += __popcll(__ballot(o[u] >= t));
+      for (int u = 4; u < nu; ++u) c += __popcll(__ballot(key(u) >= t));
+      return c;
+    };
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t t = tau | (1u << bit);
+      if (count_ge(t) >= s) tau = t;
+    }
+    int32_t above = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) above += __popcll(__ballot(o[u] > tau));
+    for (int u = 4; u < nu; ++u) above += __popcll(__ballot(key(u) > tau));
+    const int32_t need = s - above;   // keys equal to tau to keep, lowest index first
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int32_t taken = 0, cnt = 0;
+    auto emit = [&](int u, uint32_t kv) {
+      const int32_t r = lane + kWave * u;
+      const bool valid = r < C;
+      const uint64_t eq = __ballot(valid && kv == tau);
+      const bool keep = valid && (kv > tau || (kv == tau && taken + __popcll(eq & lt) < need));
+      const uint64_t km = __ballot(keep);
+      if (valid) flags[r] = keep ? 1 : 0;
+      if (keep) sel_out[cnt + __popcll(km & lt)] = cm(r);
+      taken += __popcll(eq);
+      cnt += __popcll(km);
+    };
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < nu) emit(u, o[u]);
+    for (int u = 4; u < nu; ++u) emit(u, key(u));
     wave_sync();
   };
 
   // fold entries r < cn (skipping kept ones when use_flags) into the online softmax
-  auto softmax_pv = [&](const void* vsrc, int64_t rowbase, const CandMap& cm, int64_t c0, int64_t cn,
+  auto softmax_pv = [&](const void* vsrc, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn,
                         bool use_flags) {
     float mnew[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) mnew[hh] = -INFINITY;
-    for (int64_t r = lane; r < cn; r += kWave) {
+    for (int32_t r = lane; r < cn; r += kWave) {
       if (use_flags && flags[r]) continue;
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(mnew[hh], zs[hh * zcap + r]);
@@ -355,7 +504,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
     float ls[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) ls[hh] = 0.0f;
-    for (int64_t r = lane; r < cn; r += kWave) {
+    for (int32_t r = lane; r < cn; r += kWave) {
       const bool skip = use_flags && flags[r];
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
@@ -371,27 +520,29 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
       l_run[hh] = l_run[hh] * alpha + lsum;
       m_run[hh] = mnew[hh];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
+      for (int e = 0; e < VE; ++e) acc[hh][e] *= alpha;
     }
     wave_sync();
-    for (int64_t r0 = 0; r0 < cn; r0 += RPP * PV_UNROLL) {
-      float v[PV_UNROLL][8];
+    for (int32_t r0 = 0; r0 < cn; r0 += RPP * PV_UNROLL) {
+      Raw4<BF16> raw[PV_UNROLL];
       bool live[PV_UNROLL];
 #pragma unroll
       for (int u = 0; u < PV_UNROLL; ++u) {
-        const int64_t r = r0 + u * RPP + rg;
+        const int32_t r = r0 + u * RPP + rg;
         live[u] = r < cn && !(use_flags && flags[r]);
-        if (live[u]) load8<BF16>(vsrc, (rowbase + cm(c0 + r)) * D + 8 * sub, v[u]);
+        raw[u] = live[u] ? raw4_load<BF16>(vsrc, (rowbase + cm(c0 + r)) * D + VE * sub) : raw4_zero<BF16>();
       }
 #pragma unroll
       for (int u = 0; u < PV_UNROLL; ++u) {
         if (!live[u]) continue;
-        const int64_t r = r0 + u * RPP + rg;
+        float v[VE];
+        raw4_cvt<BF16>(raw[u], v);
+        const int32_t r = r0 + u * RPP + rg;
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
           const float p = zs[hh * zcap + r];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(p, v[u][e], acc[hh][e]);
+          for (int e = 0; e < VE; ++e) acc[hh][e] = fmaf(p, v[e], acc[hh][e]);
         }
       }
     }
@@ -401,36 +552,27 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
   // --- levels T .. 1 -------------------------------------------------------------
   int32_t* sel_prev = selA;
   int32_t* sel_new = selB;
-  int64_t s_prev = 0;
+  int32_t s_prev = 0;
+  const int32_t fshift = (f & (f - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(f)) : -1;
   for (int lv = T; lv >= 1; --lv) {
-    const int64_t n_l = nls[lv], n_up = nls[lv + 1];
-    const CandMap cm{sel_prev, static_cast<int64_t>(f) * s_prev, static_cast<int64_t>(f) * n_up, f};
-    const int64_t C = cm.n_kids + (n_l - cm.orph);
-    const int64_t kl = a.k.k[lv];
-    const int64_t s = kl < C ? kl : C;
+    const int32_t n_l = static_cast<int32_t>(nls[lv]), n_up = static_cast<int32_t>(nls[lv + 1]);
+    const CandMap cm{sel_prev, f * s_prev, f * n_up, f, fshift};
+    const int32_t C = cm.n_kids + (n_l - cm.orph);
+    const int32_t kl = a.k.k[lv];
+    const int32_t s = kl < C ? kl : C;
     if (s == C) {
-      for (int64_t i = lane; i < C; i += kWave) sel_new[i] = static_cast<int32_t>(cm(i));
+      for (int32_t i = lane; i < C; i += kWave) sel_new[i] = cm(i);
       wave_sync();
     } else {
       const int64_t rowbase = bh * a.tree.rows[lv];
       rotate_query(C);
       score_rows(a.tree.NK[lv], rowbase, cm, 0, C);
       if (s > 0) {
-        select_top(C, s);
+        select_top(C, s, cm, sel_new);
       } else {
-        for (int64_t r = lane; r < C; r += kWave) flags[r] = 0;
+        for (int32_t r = lane; r < C; r += kWave) flags[r] = 0;
         wave_sync();
       }
-      int64_t cnt = 0;
-      for (int64_t base = 0; base < C; base += kWave) {
-        const int64_t i = base + lane;
-        const bool fl = i < C && flags[i];
-        const uint64_t bal = __ballot(fl);
-        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-        if (fl) sel_new[cnt + pre] = static_cast<int32_t>(cm(i));
-        cnt += __popcll(bal);
-      }
-      wave_sync();
       softmax_pv(a.tree.NV[lv], rowbase, cm, 0, C, true);
     }
     if (a.sel) {
@@ -445,17 +587,17 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
 
   // --- token level -------------------------------------------------------------------
   {
-    const int64_t n1 = T >= 1 ? nls[1] : 0;
-    const CandMap cm{sel_prev, static_cast<int64_t>(f) * s_prev, static_cast<int64_t>(f) * n1, f};
-    const int64_t C0 = cm.n_kids + (n - cm.orph);
+    const int32_t n1 = T >= 1 ? static_cast<int32_t>(nls[1]) : 0;
+    const CandMap cm{sel_prev, f * s_prev, f * n1, f, fshift};
+    const int32_t C0 = cm.n_kids + (static_cast<int32_t>(n) - cm.orph);
     const bool own = a.prefill && C0 > 0 && cm(C0 - 1) == n - 1;
-    const int64_t pq = own ? C0 - 1 : C0;
+    const int32_t pq = own ? C0 - 1 : C0;
     const int64_t rowbase = bh * a.cap;
     if (C0 > 0) rotate_query(pq);
     for (int64_t c0 = 0; c0 < C0; c0 += zcap) {
-      const int64_t cn = C0 - c0 < zcap ? C0 - c0 : zcap;
-      score_rows(a.K, rowbase, cm, c0, cn);
-      softmax_pv(a.V, rowbase, cm, c0, cn, false);
+      const int32_t cn = static_cast<int32_t>(C0 - c0 < zcap ? C0 - c0 : zcap);
+      score_rows(a.K, rowbase, cm, static_cast<int32_t>(c0), cn);
+      softmax_pv(a.V, rowbase, cm, static_cast<int32_t>(c0), cn, false);
     }
   }
 
@@ -465,16 +607,15 @@ __global__ __launch_bounds__(64) void attend_kernel(AttnArgs a) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], off);
+      for (int e = 0; e < VE; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], off);
   const int64_t obase = ((b * a.n_q + j) * a.Hq + static_cast<int64_t>(h) * G) * D;
   if (rg == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const float l = l_run[hh];
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      float4* o = reinterpret_cast<float4*>(a.out + obase + hh * D + 8 * sub);
+      float4* o = reinterpret_cast<float4*>(a.out + obase + hh * D + VE * sub);
       o[0] = make_float4(acc[hh][0] * inv, acc[hh][1] * inv, acc[hh][2] * inv, acc[hh][3] * inv);
-      o[1] = make_float4(acc[hh][4] * inv, acc[hh][5] * inv, acc[hh][6] * inv, acc[hh][7] * inv);
     }
   }
   if (a.lse) {
