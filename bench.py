@@ -100,14 +100,13 @@ def build_bytes(w):
 
 
 def pool_launches(w):
-    """Pool-kernel launches of one full build: the library builds two levels per launch when one
-    tile of pooled nodes is exactly one parent's children (f = 16 at d = 128, f = 32 at d = 64),
-    else one level."""
+    """Pool-kernel launches of one full build: the library builds two levels per launch when
+    the fanout divides the nodes of one tile (32 at d = 128, 64 at d = 64), else one level."""
     T, m = 0, w.L // w.f
     while m >= 1:
         T += 1
         m //= w.f
-    fused = (w.d, w.f) in ((128, 16), (64, 32))
+    fused = {128: 32, 64: 64}[w.d] % w.f == 0
     return (T + 1) // 2 if fused else T
 
 

@@ -304,7 +304,7 @@ int32_t recsa_build_tree(const recsa_shape_t* shape, const void* K, const void* 
     return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int Tc = levels_of(I.cap, I.f);
-  const bool can_fuse = I.f == recsa::pool_nodes_per_tile(static_cast<int>(I.d));
+  const bool can_fuse = recsa::pool_nodes_per_tile(static_cast<int>(I.d)) % I.f == 0;
   for (int lv = 1; lv <= T;) {
     const int64_t lo = nodes_at(n_old, I.f, lv), hi = nodes_at(n_new, I.f, lv);
     const bool fuse = can_fuse && lv + 1 <= Tc;

@@ -6,7 +6,7 @@
 // value. Here the pooler is key = W @ m, m the mean of the node's f children's
 // stored keys; the value is the mean of the children's stored values.
 //
-// HBM-bound: a tile reads f * (rows per tile) child rows of K and V once and
+// HBM-bound: a tile reads f * (nodes per tile) child rows of K and V once and
 // writes 1/f as many node rows. Each workgroup keeps W (transposed, float32)
 // in LDS and loops over tiles, so W is fetched once per workgroup.
 //
@@ -56,30 +56,33 @@ struct Chunk<false> {
 
 template <int D>
 struct PoolGeom {
+  static constexpr int T = 512;           // threads per workgroup
   static constexpr int CH = D / 8;        // 8-element chunks per row (phase 1)
-  static constexpr int NPW = 256 / CH;    // nodes per tile: 16 (d=128) / 32 (d=64)
+  static constexpr int NPW = T / CH;      // nodes per tile: 32 (d=128) / 64 (d=64)
   static constexpr int OG = D / 4;        // groups of 4 outputs (phase 2)
-  static constexpr int NGR = 256 / OG;    // node groups
+  static constexpr int NGR = T / OG;      // node groups
   static constexpr int NPT = NPW / NGR;   // nodes per thread
 };
 
 // One pass over level-l nodes [g_lo, g_hi) of every (sequence, KV head); tiles of NPW
-// nodes aligned to multiples of NPW. Each thread prefetches its next tile's children into
-// registers before the matrix-vector phase of the current one, so loads stay in flight.
-// With FUSE (f == NPW) the tile's parent at level l+1 is built from the tile's nodes too
-// (reading already-stored nodes below g_lo back from the tree).
+// nodes aligned to multiples of NPW. Phase 1: a thread sums one 8-element chunk of one
+// node's children in child order; the first PF children of its next tile are loaded into
+// registers before the matrix-vector phase of the current tile, the rest in batches of PF.
+// Phase 2: W @ m for the tile's nodes from LDS. With FUSE (f divides NPW) the tile holds
+// NPW / f whole parents at level l+1, which are built in the same pass from the tile's node
+// rows as stored (re-read through the cache in 16-byte chunks; rows below g_lo come from
+// earlier calls).
+// Two workgroups of 512 threads per CU (W and the tile's key means fill the LDS), at most
+// 128 VGPRs each.
 template <int D, bool BF16, bool FUSE>
-__global__ __launch_bounds__(256, 2) void pool_kernel(PoolArgs a) {
+__global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
   using Gm = PoolGeom<D>;
-  constexpr int CH = Gm::CH, NPW = Gm::NPW, NPT = Gm::NPT;
-  constexpr int PF = BF16 ? 16 : 8;       // children held in registers per thread
-  using ST = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int T = Gm::T, CH = Gm::CH, NPW = Gm::NPW, NPT = Gm::NPT;
+  constexpr int PF = BF16 ? 2 : 1;        // children per register batch
   static_assert(NPT == 2, "phase 2 tiles 4 outputs x 2 nodes per thread");
   __shared__ float wt[D][D];              // wt[j][i] = W[i][j], float32
   __shared__ float mt[D][NPW];            // mt[j][node] = mean of the node's child keys
-  __shared__ ST k1s[FUSE ? NPW : 1][D];   // this tile's node keys / values (storage values)
-  __shared__ ST v1s[FUSE ? NPW : 1][D];
-  float* const m2s = &mt[0][0];           // the parent's key mean reuses mt after phase 2
+  float* const m2s = &mt[0][0];           // parents' key means [P][D] reuse mt after phase 2
 
   const int tid = threadIdx.x;
   const int f = a.f;
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void pool_kernel(PoolArgs a) {
   const int64_t tiles_per_bh = (a.g_hi - base0 + NPW - 1) / NPW;
   const int64_t total = tiles_per_bh * a.BH;
 
-  for (int idx = tid; idx < D * CH; idx += 256) {
+  for (int idx = tid; idx < D * CH; idx += T) {
     const int i = idx / CH, j0 = (idx % CH) * 8;
     float x[8];
     load8<BF16>(a.W, static_cast<int64_t>(i) * D + j0, x);
@@ -125,10 +128,9 @@ __global__ __launch_bounds__(256, 2) void pool_kernel(PoolArgs a) {
     const int64_t bh = tile / tiles_per_bh;
     const int64_t tb = base0 + (tile % tiles_per_bh) * NPW;
     const int64_t g = tb + nl;
-    const bool fresh = g >= a.g_lo && g < a.g_hi;
 
     // phase 1: child sums in child order -> node value (stored) and key mean (LDS)
-    if (fresh) {
+    if (g >= a.g_lo && g < a.g_hi) {
       float sk[8], sv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) { sk[e] = 0.0f; sv[e] = 0.0f; }
@@ -140,12 +142,22 @@ __global__ __launch_bounds__(256, 2) void pool_kernel(PoolArgs a) {
         }
       }
       const int64_t cb = (bh * a.src_rows + g * f) * D + ch * 8;
-      for (int c = PF; c < f; ++c) {
-        Chunk<BF16> xk, xv;
-        xk.load(a.srcK, cb + static_cast<int64_t>(c) * D);
-        xv.load(a.srcV, cb + static_cast<int64_t>(c) * D);
-        xk.add_to(sk);
-        xv.add_to(sv);
+      for (int c0 = PF; c0 < f; c0 += PF) {
+        Chunk<BF16> xk[PF], xv[PF];
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          if (c0 + u < f) {
+            xk[u].load(a.srcK, cb + static_cast<int64_t>(c0 + u) * D);
+            xv[u].load(a.srcV, cb + static_cast<int64_t>(c0 + u) * D);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          if (c0 + u < f) {
+            xk[u].add_to(sk);
+            xv[u].add_to(sv);
+          }
+        }
       }
       float nv[8];
 #pragma unroll
@@ -154,29 +166,6 @@ __global__ __launch_bounds__(256, 2) void pool_kernel(PoolArgs a) {
         nv[e] = round_store<BF16>(div_f(sv[e]));
       }
       store8<BF16>(a.dstV, (bh * a.dst_rows + g) * D + ch * 8, nv);
-      if constexpr (FUSE) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if constexpr (BF16) v1s[nl][ch * 8 + e] = static_cast<uint16_t>(__float_as_uint(nv[e]) >> 16);
-          else v1s[nl][ch * 8 + e] = nv[e];
-        }
-      }
-    } else if (FUSE && g < a.g_lo) {
-      // node built by an earlier call: its stored key and value feed the parent
-      const int64_t off = (bh * a.dst_rows + g) * D + ch * 8;
-      float xk[8], xv[8];
-      load8<BF16>(a.dstK, off, xk);
-      load8<BF16>(a.dstV, off, xv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (BF16) {
-          k1s[nl][ch * 8 + e] = static_cast<uint16_t>(__float_as_uint(xk[e]) >> 16);
-          v1s[nl][ch * 8 + e] = static_cast<uint16_t>(__float_as_uint(xv[e]) >> 16);
-        } else {
-          k1s[nl][ch * 8 + e] = xk[e];
-          v1s[nl][ch * 8 + e] = xv[e];
-        }
-      }
     }
     __syncthreads();
     prefetch(tile + gridDim.x);
@@ -208,50 +197,56 @@ __global__ __launch_bounds__(256, 2) void pool_kernel(PoolArgs a) {
           const uint32_t b0 = f32_to_bf16_bits(acc[u][0]), b1 = f32_to_bf16_bits(acc[u][1]);
           const uint32_t b2 = f32_to_bf16_bits(acc[u][2]), b3 = f32_to_bf16_bits(acc[u][3]);
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dstK) + off) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-          if constexpr (FUSE) {
-            k1s[n0 + u][o0] = b0; k1s[n0 + u][o0 + 1] = b1; k1s[n0 + u][o0 + 2] = b2; k1s[n0 + u][o0 + 3] = b3;
-          }
         } else {
           *reinterpret_cast<float4*>(static_cast<float*>(a.dstK) + off) =
               make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
-          if constexpr (FUSE) {
-#pragma unroll
-            for (int o = 0; o < 4; ++o) k1s[n0 + u][o0 + o] = acc[u][o];
-          }
         }
       }
     }
 
     if constexpr (FUSE) {
-      // the tile's parent one level up: children = the NPW (= f) node slots of this tile
-      const int64_t g2 = tb / NPW;
-      if (g2 >= a.g_lo / NPW && g2 < a.g_hi / NPW) {
-        __syncthreads();
-        if (tid < 2 * D) {
-          const int dd = tid % D;
-          float s = 0.0f;
-          if (tid < D) {
-#pragma unroll 4
-            for (int c = 0; c < NPW; ++c) {
-              if constexpr (BF16) s = s + bf16_to_f32(k1s[c][dd]);
-              else s = s + k1s[c][dd];
-            }
-            m2s[dd] = div_f(s);
+      // the tile's parents one level up, [pb, pb + P), those in [g_lo / f, g_hi / f)
+      const int P = NPW / f;
+      const int64_t p_lo = a.g_lo / f, p_hi = a.g_hi / f, pb = tb / f;
+      if (pb + P > p_lo && pb < p_hi) {
+        __syncthreads();   // the tile's node rows are stored and visible to the workgroup
+        for (int it = tid; it < P * 2 * CH; it += T) {
+          const int p = it / (2 * CH), rem = it % (2 * CH), which = rem / CH, cc = rem % CH;
+          const int64_t g2 = pb + p;
+          if (g2 < p_lo || g2 >= p_hi) continue;
+          const void* src = which ? a.dstV : a.dstK;
+          const int64_t rb = (bh * a.dst_rows + g2 * f) * D + cc * 8;
+          float s8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s8[e] = 0.0f;
+          for (int c0 = 0; c0 < f; c0 += 4) {
+            Chunk<BF16> x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (c0 + u < f) x[u].load(src, rb + static_cast<int64_t>(c0 + u) * D);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (c0 + u < f) x[u].add_to(s8);
+          }
+          if (which == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m2s[p * D + cc * 8 + e] = div_f(s8[e]);
           } else {
-#pragma unroll 4
-            for (int c = 0; c < NPW; ++c) {
-              if constexpr (BF16) s = s + bf16_to_f32(v1s[c][dd]);
-              else s = s + v1s[c][dd];
-            }
-            store1<BF16>(a.dst2V, (bh * a.dst2_rows + g2) * D + dd, round_store<BF16>(div_f(s)));
+            float o8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o8[e] = round_store<BF16>(div_f(s8[e]));
+            store8<BF16>(a.dst2V, (bh * a.dst2_rows + g2) * D + cc * 8, o8);
           }
         }
         __syncthreads();
-        if (tid < D) {
+        for (int it = tid; it < P * D; it += T) {
+          const int p = it / D, i = it % D;
+          const int64_t g2 = pb + p;
+          if (g2 < p_lo || g2 >= p_hi) continue;
           float acc2 = 0.0f;
 #pragma unroll 8
-          for (int j = 0; j < D; ++j) acc2 = fmaf(wt[j][tid], m2s[j], acc2);
-          store1<BF16>(a.dst2K, (bh * a.dst2_rows + g2) * D + tid, round_store<BF16>(acc2));
+          for (int j = 0; j < D; ++j) acc2 = fmaf(wt[j][i], m2s[p * D + j], acc2);
+          store1<BF16>(a.dst2K, (bh * a.dst2_rows + g2) * D + i, round_store<BF16>(acc2));
         }
       }
     }
@@ -270,7 +265,7 @@ static int persistent_grid() {
     else
       cus = 256;
   }
-  return 2 * cus;  // two 256-thread workgroups fit a CU's LDS
+  return 2 * cus;  // two 512-thread workgroups fit a CU's LDS
 }
 
 template <int D, bool BF16>
@@ -282,9 +277,9 @@ static hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
   const int64_t cap = a.grid > 0 ? a.grid : persistent_grid();
   const int64_t grid = tiles < cap ? tiles : cap;
   if (a.fuse_next) {
-    hipLaunchKernelGGL((pool_kernel<D, BF16, true>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pool_kernel<D, BF16, true>), dim3(static_cast<unsigned>(grid)), dim3(PoolGeom<D>::T), 0, s, a);
   } else {
-    hipLaunchKernelGGL((pool_kernel<D, BF16, false>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pool_kernel<D, BF16, false>), dim3(static_cast<unsigned>(grid)), dim3(PoolGeom<D>::T), 0, s, a);
   }
   return hipGetLastError();
 }

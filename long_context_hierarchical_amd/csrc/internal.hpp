@@ -21,15 +21,15 @@ struct PoolArgs {
   int64_t g_lo, g_hi;   // node range to build
   int32_t f;
   int32_t BH;           // batch * n_kv_heads
-  // Optional fused next level (f == nodes per tile): the level-(l+1) nodes whose children
-  // all fall in one tile are built in the same pass, nodes [g_lo / f, g_hi / f).
+  // Optional fused next level (f divides the nodes per tile): the level-(l+1) nodes, whose
+  // children all fall in one tile, are built in the same pass, nodes [g_lo / f, g_hi / f).
   int32_t fuse_next;
   void* dst2K;
   void* dst2V;
   int64_t dst2_rows;
   int32_t grid;         // persistent grid size (0 = library default)
 };
-// Nodes per tile of the pool kernel (= the fanout for which the next level can be fused).
+// Nodes per tile of the pool kernel (the next level is fused when the fanout divides it).
 int pool_nodes_per_tile(int d);
 hipError_t launch_pool_level(const PoolArgs& a, int d, bool bf16, hipStream_t s);
 
