@@ -36,7 +36,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-units", type=int, default=24, help="oracle decode units timed for the baseline")
     ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--step-mode", action="store_true", help="also time one-query-per-sequence decode calls")
+    ap.add_argument("--no-step-mode", action="store_true", help="skip timing one-query-per-sequence decode calls")
+    ap.add_argument("--no-library-legs", action="store_true",
+                    help="skip the library flash-attention comparison (torch scaled_dot_product_attention)")
     ap.add_argument("--no-legs", action="store_true", help="skip the dense and prefill comparison legs")
     ap.add_argument("--prefill-chunk", type=int, default=4096)
     return ap.parse_args()
@@ -108,6 +110,54 @@ def pool_launches(w):
         m //= w.f
     fused = {128: 32, 64: 64}[w.d] % w.f == 0
     return (T + 1) // 2 if fused else T
+
+
+def library_legs(w, Kr, V, q, qp, c, timed):
+    """The same dense attention through torch.nn.functional.scaled_dot_product_attention (the
+    platform's flash-attention library), timing only: the KV heads are expanded to the query
+    heads first and the queries are used as stored (no rotation), so outputs are not compared.
+    Records the backend used, or the error if no fused backend accepts the shapes."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    G = w.Hq // w.Hkv
+    out = {}
+    try:
+        Ke = Kr.repeat_interleave(G, dim=1)        # [B][Hq][L][d]
+        Ve = V.repeat_interleave(G, dim=1)
+    except RuntimeError as e:                      # out of memory
+        return {"error": str(e)[:200]}
+    qd = q.transpose(1, 2).contiguous()            # [B][Hq][n_q][d]
+    qs = q[:, :1].transpose(1, 2).contiguous()
+    qpre = qp.transpose(1, 2).contiguous()         # [B][Hq][c][d]
+    for backend in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:
+            with sdpa_kernel(backend):
+                ms_b = timed(lambda: F.scaled_dot_product_attention(qd, Ke, Ve), 3)
+                ms_s = timed(lambda: F.scaled_dot_product_attention(qs, Ke, Ve), 10)
+            out = {"backend": backend.name,
+                   "decode_batched_ms": round(ms_b, 4),
+                   "decode_batched_queries_per_s": round(w.B * w.n_queries / (ms_b * 1e-3), 1),
+                   "decode_batched_TFLOPs": round(4.0 * w.B * w.n_queries * w.Hq * w.d * w.L / (ms_b * 1e-3) / 1e12, 1),
+                   "decode_step_ms": round(ms_s, 4),
+                   "decode_step_GBps": round(2 * w.B * w.Hkv * w.L * w.d * w.elem_bytes / (ms_s * 1e-3) / 1e9, 1)}
+            break
+        except RuntimeError as e:
+            out = {"error": f"{backend.name}: {str(e)[:200]}"}
+    if "backend" in out:
+        try:
+            from torch.nn.attention.bias import causal_lower_right
+            mask = causal_lower_right(c, w.L)
+            with sdpa_kernel(getattr(SDPBackend, out["backend"])):
+                ms_p = timed(lambda: F.scaled_dot_product_attention(qpre, Ke, Ve, attn_mask=mask), 2)
+            flops = 4.0 * w.B * w.Hq * w.d * sum(range(w.L - c + 1, w.L + 1))
+            out["prefill_last_chunk_ms"] = round(ms_p, 4)
+            out["prefill_last_chunk_TFLOPs"] = round(flops / (ms_p * 1e-3) / 1e12, 1)
+        except (RuntimeError, ImportError, TypeError) as e:
+            out["prefill_error"] = str(e)[:200]
+    del Ke, Ve
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, k, n_units):
@@ -317,10 +367,13 @@ def main():
         legs["speedup_decode_batched"] = round(legs["dense_decode_batched"]["ms_per_call"] / decode_ms, 2)
         legs["speedup_prefill_last_chunk"] = round(legs["dense_prefill_last_chunk"]["ms_per_call"] /
                                                    legs["recsa_prefill_last_chunk"]["ms_per_call"], 2)
+        if not args.no_library_legs:
+            log("library flash-attention legs (timing only)")
+            legs["library_sdpa"] = library_legs(w, Kr, V, q, qp, c, timed)
         del Kr
         res["breakdown"]["legs"] = legs
 
-    if args.step_mode:
+    if not args.no_step_mode:
         one_q = q[:, :1].contiguous()
         o1 = torch.empty(w.B, 1, w.Hq, w.d, dtype=torch.float32, device=dev)
         for _ in range(3):
