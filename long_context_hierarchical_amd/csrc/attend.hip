@@ -76,7 +76,7 @@ __device__ __forceinline__ void load4(const void* base, int64_t off, float (&x)[
 }
 
 struct Lds {
-  uint32_t q, qr, zs, sc, flags, selA, selB, nls, total;
+  uint32_t q, qr, zs, sc, flags, selA, selB, nls, bc, total;
 };
 
 __host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
@@ -92,6 +92,7 @@ __host__ __device__ inline Lds lds_layout(int d, int G, int smax, int zcap) {
   L.selA = o;  o = align16(o + 4u * smax);          // kept node ids, two buffers
   L.selB = o;  o = align16(o + 4u * smax);
   L.nls = o;   o = align16(o + 8u * (RECSA_MAX_LEVELS + 2));
+  L.bc = o;    o = align16(o + 4u * 2 * G);           // softmax rescale and sum, wave 0 -> all
   L.total = o;
   return L;
 }
@@ -213,15 +214,56 @@ __device__ __forceinline__ void raw4_cvt(const Raw4<BF16>& r, float (&x)[4]) {
   }
 }
 
-template <int D, bool BF16, int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void attend_kernel(AttnArgs a) {
-  constexpr int VE = 4;                // elements per lane, value phase
+// One value-row fragment of N (1, 2 or 4) storage elements, as loaded.
+template <bool BF16, int N>
+struct RawV {
+  using T = typename std::conditional<
+      BF16, typename std::conditional<N == 4, uint2, typename std::conditional<N == 2, uint32_t, uint16_t>::type>::type,
+      typename std::conditional<N == 4, uint4, typename std::conditional<N == 2, uint2, uint32_t>::type>::type>::type;
+  T u;
+  __device__ __forceinline__ void load(const void* base, int64_t off) {
+    if constexpr (BF16) u = *reinterpret_cast<const T*>(static_cast<const uint16_t*>(base) + off);
+    else u = *reinterpret_cast<const T*>(static_cast<const float*>(base) + off);
+  }
+  __device__ __forceinline__ void zero() { u = T{}; }
+  __device__ __forceinline__ void cvt(float (&x)[N]) const {
+    if constexpr (BF16) {
+      if constexpr (N == 4) {
+        x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xFFFF0000u);
+        x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+      } else if constexpr (N == 2) {
+        x[0] = __uint_as_float(u << 16); x[1] = __uint_as_float(u & 0xFFFF0000u);
+      } else {
+        x[0] = __uint_as_float(static_cast<uint32_t>(u) << 16);
+      }
+    } else {
+      if constexpr (N == 4) {
+        x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y); x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+      } else if constexpr (N == 2) {
+        x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+      } else {
+        x[0] = __uint_as_float(u);
+      }
+    }
+  }
+};
+
+// NW waves per unit. NW = 1: one wave does everything. NW > 1 (few units, latency-bound):
+// the waves share the score passes, wave 0 alone selects and computes the softmax weights,
+// and each wave owns D / NW of the value dimensions with the same row-group accumulation
+// chains as one wave, so every output element is accumulated in exactly the same order and
+// the results are bitwise those of NW = 1.
+template <int D, bool BF16, int G, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void attend_kernel(AttnArgs a) {
+  constexpr int VE = 4;                // elements per row group lane (one wave), value phase
+  constexpr int VEW = VE / NW;         // elements per lane of each wave
   constexpr int RL = D / VE;           // lanes per row, value phase
   constexpr int RPP = kWave / RL;      // rows per pass, value phase
   constexpr int SL = D / 16;           // lanes per row, score phase (8 rotate-half pairs per lane)
   constexpr int SPP = kWave / SL;      // rows per pass, score phase
   constexpr int HALF = D / 2;
-  constexpr int PV_UNROLL = 4;
+  constexpr int PV_UNROLL = NW == 1 ? 4 : 16;
+  static_assert(VE % NW == 0, "waves split the value elements of a lane");
 
   extern __shared__ __align__(16) unsigned char lds[];
   const int zcap = a.zcap;
@@ -236,8 +278,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
   int32_t* selA = reinterpret_cast<int32_t*>(lds + L.selA);
   int32_t* selB = reinterpret_cast<int32_t*>(lds + L.selB);
   int64_t* nls = reinterpret_cast<int64_t*>(lds + L.nls);
+  float* bc = reinterpret_cast<float*>(lds + L.bc);   // wave 0 -> all: alpha[G], l[G]
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  const int tid = threadIdx.x;
+  constexpr int NT = NW * kWave;
+  auto bsync = [&]() {
+    if constexpr (NW == 1) wave_sync();
+    else __syncthreads();
+  };
   const int sub = lane % RL, rg = lane / RL;       // value phase
   const int ssub = lane % SL, srg = lane / SL;     // score phase
   const int64_t unit = blockIdx.x;
@@ -251,13 +300,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
   // raw query heads of the KV group -> LDS (float)
   {
     const int64_t qbase = ((b * a.n_q + j) * a.Hq + static_cast<int64_t>(h) * G) * D;
-    for (int i = lane * 4; i < G * D; i += kWave * 4) {
+    for (int i = tid * 4; i < G * D; i += NT * 4) {
       float x[4];
       load4<BF16>(a.q, qbase + i, x);
       *reinterpret_cast<float4*>(qs + i) = make_float4(x[0], x[1], x[2], x[3]);
     }
   }
-  if (lane == 0) {
+  if (tid == 0) {
     int T = 0;
     int64_t m = n / f;
     while (m >= 1 && T < RECSA_MAX_LEVELS) {
@@ -267,21 +316,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
     nls[T + 1] = 0;
     nls[0] = T;
   }
-  wave_sync();
+  bsync();
   const int T = static_cast<int>(nls[0]);
   const int64_t sel_row0 = ((b * a.n_q + j) * a.Hkv + h) * a.n_levels;
   if (a.sel) {
     for (int lv = T + 1; lv <= a.n_levels; ++lv)
-      for (int c = lane; c < a.sel_width; c += kWave) a.sel[(sel_row0 + lv - 1) * a.sel_width + c] = -1;
+      for (int c = tid; c < a.sel_width; c += NT) a.sel[(sel_row0 + lv - 1) * a.sel_width + c] = -1;
   }
 
-  float m_run[G], l_run[G], acc[G][VE];
+  float m_run[G], l_run[G], acc[G][VEW];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     m_run[hh] = -INFINITY;
     l_run[hh] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) acc[hh][e] = 0.0f;
+    for (int e = 0; e < VEW; ++e) acc[hh][e] = 0.0f;
   }
 
   // rotated query operands for the current level -> qr: lane slot ssub holds the 8
@@ -320,7 +369,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
         }
       }
       uint32_t* dst = qr + (hh * SL + ssub) * 16;
-      if (srg == 0) {
+      if (srg == 0 && wid == 0) {
         if constexpr (BF16) {
           uint32_t w[8];
 #pragma unroll
@@ -338,7 +387,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
         }
       }
     }
-    wave_sync();
+    bsync();
   };
 
   // logits of candidates [c0, c0 + cn) (index = RoPE position) -> zs[hh * zcap + r], sc[r]
@@ -356,15 +405,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
       }
     };
     Raw8<BF16> nlo, nhi;
-    fetch(0, nlo, nhi);
-    for (int32_t r0 = 0; r0 < cn; r0 += SPP) {
+    fetch(wid * SPP, nlo, nhi);
+    for (int32_t r0 = wid * SPP; r0 < cn; r0 += NW * SPP) {
       const int32_t r = r0 + srg;
       const bool valid = r < cn;
       const int32_t i = c0 + r;
       float klo[8], khi[8];
       raw8_cvt<BF16>(nlo, klo);
       raw8_cvt<BF16>(nhi, khi);
-      if (r0 + SPP < cn) fetch(r0 + SPP, nlo, nhi);
+      if (r0 + NW * SPP < cn) fetch(r0 + NW * SPP, nlo, nhi);
       float olo[8], ohi[8];
       if (a.use_rope) {
         const float4* t = reinterpret_cast<const float4*>(a.tab + static_cast<int64_t>(valid ? i : 0) * HALF + 8 * ssub);
@@ -431,7 +480,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
         sc[r] = S;
       }
     }
-    wave_sync();
+    bsync();
   };
 
   // Keeps the s largest (S, -r) keys among r < C: flags[r] = 1 and sel_out[0..s) = their
@@ -488,65 +537,88 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
     wave_sync();
   };
 
-  // fold entries r < cn (skipping kept ones when use_flags) into the online softmax
+  // fold entries r < cn (skipping kept ones when use_flags) into the online softmax: wave 0
+  // computes the weights (into zs) and the running max and sum; every wave then accumulates
+  // its value elements
+  const int dim0 = wid * (D / NW) + sub * VEW;
   auto softmax_pv = [&](const void* vsrc, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn,
                         bool use_flags) {
-    float mnew[G];
+    if (wid == 0) {
+      float mnew[G];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) mnew[hh] = -INFINITY;
-    for (int32_t r = lane; r < cn; r += kWave) {
-      if (use_flags && flags[r]) continue;
+      for (int hh = 0; hh < G; ++hh) mnew[hh] = -INFINITY;
+      for (int32_t r = lane; r < cn; r += kWave) {
+        if (use_flags && flags[r]) continue;
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(mnew[hh], zs[hh * zcap + r]);
-    }
+        for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(mnew[hh], zs[hh * zcap + r]);
+      }
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(m_run[hh], wave_max(mnew[hh]));
-    float ls[G];
+      for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(m_run[hh], wave_max(mnew[hh]));
+      float ls[G];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) ls[hh] = 0.0f;
-    for (int32_t r = lane; r < cn; r += kWave) {
-      const bool skip = use_flags && flags[r];
+      for (int hh = 0; hh < G; ++hh) ls[hh] = 0.0f;
+      for (int32_t r = lane; r < cn; r += kWave) {
+        const bool skip = use_flags && flags[r];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float p = skip ? 0.0f : expf(zs[hh * zcap + r] - mnew[hh]);
+          zs[hh * zcap + r] = p;
+          ls[hh] += p;
+        }
+      }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const float p = skip ? 0.0f : expf(zs[hh * zcap + r] - mnew[hh]);
-        zs[hh * zcap + r] = p;
-        ls[hh] += p;
+        const float lsum = wave_sum(ls[hh]);
+        const float alpha = expf(m_run[hh] - mnew[hh]);
+        l_run[hh] = l_run[hh] * alpha + lsum;
+        m_run[hh] = mnew[hh];
+#pragma unroll
+        for (int e = 0; e < VEW; ++e) acc[hh][e] *= alpha;
+        if constexpr (NW > 1) {
+          if (lane == 0) {
+            bc[hh] = alpha;
+            bc[G + hh] = l_run[hh];
+          }
+        }
       }
     }
+    bsync();
+    if constexpr (NW > 1) {
+      if (wid != 0) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float lsum = wave_sum(ls[hh]);
-      const float alpha = expf(m_run[hh] - mnew[hh]);
-      l_run[hh] = l_run[hh] * alpha + lsum;
-      m_run[hh] = mnew[hh];
+        for (int hh = 0; hh < G; ++hh) {
+          const float alpha = bc[hh];
+          l_run[hh] = bc[G + hh];
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc[hh][e] *= alpha;
+          for (int e = 0; e < VEW; ++e) acc[hh][e] *= alpha;
+        }
+      }
     }
-    wave_sync();
     for (int32_t r0 = 0; r0 < cn; r0 += RPP * PV_UNROLL) {
-      Raw4<BF16> raw[PV_UNROLL];
+      RawV<BF16, VEW> raw[PV_UNROLL];
       bool live[PV_UNROLL];
 #pragma unroll
       for (int u = 0; u < PV_UNROLL; ++u) {
         const int32_t r = r0 + u * RPP + rg;
         live[u] = r < cn && !(use_flags && flags[r]);
-        raw[u] = live[u] ? raw4_load<BF16>(vsrc, (rowbase + cm(c0 + r)) * D + VE * sub) : raw4_zero<BF16>();
+        if (live[u]) raw[u].load(vsrc, (rowbase + cm(c0 + r)) * D + dim0);
+        else raw[u].zero();
       }
 #pragma unroll
       for (int u = 0; u < PV_UNROLL; ++u) {
         if (!live[u]) continue;
-        float v[VE];
-        raw4_cvt<BF16>(raw[u], v);
+        float v[VEW];
+        raw[u].cvt(v);
         const int32_t r = r0 + u * RPP + rg;
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
           const float p = zs[hh * zcap + r];
 #pragma unroll
-          for (int e = 0; e < VE; ++e) acc[hh][e] = fmaf(p, v[e], acc[hh][e]);
+          for (int e = 0; e < VEW; ++e) acc[hh][e] = fmaf(p, v[e], acc[hh][e]);
         }
       }
     }
-    wave_sync();
+    bsync();
   };
 
   // --- levels T .. 1 -------------------------------------------------------------
@@ -561,22 +633,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
     const int32_t kl = a.k.k[lv];
     const int32_t s = kl < C ? kl : C;
     if (s == C) {
-      for (int32_t i = lane; i < C; i += kWave) sel_new[i] = cm(i);
-      wave_sync();
+      for (int32_t i = tid; i < C; i += NT) sel_new[i] = cm(i);
+      bsync();
     } else {
       const int64_t rowbase = bh * a.tree.rows[lv];
       rotate_query(C);
       score_rows(a.tree.NK[lv], rowbase, cm, 0, C);
       if (s > 0) {
-        select_top(C, s, cm, sel_new);
+        if (wid == 0) select_top(C, s, cm, sel_new);
       } else {
-        for (int32_t r = lane; r < C; r += kWave) flags[r] = 0;
-        wave_sync();
+        for (int32_t r = tid; r < C; r += NT) flags[r] = 0;
       }
+      bsync();
       softmax_pv(a.tree.NV[lv], rowbase, cm, 0, C, true);
     }
     if (a.sel) {
-      for (int c = lane; c < a.sel_width; c += kWave)
+      for (int c = tid; c < a.sel_width; c += NT)
         a.sel[(sel_row0 + lv - 1) * a.sel_width + c] = c < s ? sel_new[c] : -1;
     }
     int32_t* t = sel_prev;
@@ -607,18 +679,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int e = 0; e < VE; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], off);
+      for (int e = 0; e < VEW; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], off);
   const int64_t obase = ((b * a.n_q + j) * a.Hq + static_cast<int64_t>(h) * G) * D;
   if (rg == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const float l = l_run[hh];
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      float4* o = reinterpret_cast<float4*>(a.out + obase + hh * D + VE * sub);
-      o[0] = make_float4(acc[hh][0] * inv, acc[hh][1] * inv, acc[hh][2] * inv, acc[hh][3] * inv);
+      float* o = a.out + obase + hh * D + dim0;
+      if constexpr (VEW == 4) {
+        *reinterpret_cast<float4*>(o) = make_float4(acc[hh][0] * inv, acc[hh][1] * inv, acc[hh][2] * inv, acc[hh][3] * inv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEW; ++e) o[e] = acc[hh][e] * inv;
+      }
     }
   }
-  if (a.lse) {
+  if (a.lse && wid == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       if (lane == hh) {
@@ -629,10 +706,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
   }
 }
 
+// Units (sequence, query, KV head) below which a unit gets several waves: with fewer, the
+// GPU is not filled by one wave per unit and the descent's latency dominates.
+constexpr int64_t kMultiWaveUnits = 2048;
+
 template <int D, bool BF16, int G>
 static hipError_t launch_attend_t(const AttnArgs& a, size_t lds, int64_t B, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.n_q * a.Hkv), static_cast<unsigned>(B));
-  hipLaunchKernelGGL((attend_kernel<D, BF16, G>), grid, dim3(kWave), lds, s, a);
+  if (a.n_q * a.Hkv * B < kMultiWaveUnits) {
+    hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds, s, a);
+  } else {
+    hipLaunchKernelGGL((attend_kernel<D, BF16, G, 1>), grid, dim3(kWave), lds, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -168,6 +168,22 @@ def test_decode_is_deterministic():
     assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
 
 
+def test_decode_launch_shapes_agree_bitwise():
+    """Calls with many units run one wave per (sequence, query, KV head); calls with few run
+    several waves per unit. Both accumulate every output element in the same order, so the
+    same query gives bitwise-identical results either way."""
+    w = _w("shapes", B=2, Hq=32, Hkv=8, d=128, dtype="bf16", L=70000, k=8, n_queries=150, seed=23)
+    inp = gen_decode_inputs(w)
+    g = Gpu(w, inp)
+    k = [8] * 4
+    big = g.decode(k, w.L)                      # 2 x 150 x 8 = 2400 units: one wave each
+    for j in (0, 77, 149):
+        one = g.decode(k, w.L, q=g.q[:, j:j + 1].contiguous())   # 16 units: several waves each
+        assert np.array_equal(one[2][:, 0], big[2][:, j]), j
+        assert np.array_equal(one[0][:, 0].view(np.uint32), big[0][:, j].view(np.uint32)), j
+        assert np.array_equal(one[1][:, 0].view(np.uint32), big[1][:, j].view(np.uint32)), j
+
+
 # ------------------------------------------------------------------ prefill
 
 def test_prefill_matches_oracle_and_chunking():
