@@ -112,6 +112,26 @@ def pool_launches(w):
     return (T + 1) // 2 if fused else T
 
 
+def tile_sharing(sel):
+    """How many (query, KV head) units of one call share each candidate tile: at level l the
+    children of the level-(l+1) node kept at rank r form one tile of keys rotated at the same
+    positions, shared by every unit that kept that node at that rank. sel: [B][n_q][H_kv][T][w]."""
+    import numpy as np
+    B, nq, H, T, width = sel.shape
+    out = {}
+    for lv in range(T, 0, -1):                        # parents kept at level lv -> tiles at lv - 1
+        s = sel[:, :, :, lv - 1, :]
+        bb, _, hh, rr = np.nonzero(s >= 0)
+        if bb.size == 0:
+            continue
+        node = s[s >= 0].astype(np.int64)
+        key = ((bb.astype(np.int64) * H + hh) * (int(node.max()) + 1) + node) * width + rr
+        tiles = np.unique(key).size
+        out[f"level_{lv - 1}"] = {"unit_tiles": int(bb.size), "distinct_tiles": int(tiles),
+                                  "units_per_tile": round(bb.size / tiles, 2)}
+    return out
+
+
 def library_legs(w, Kr, V, q, qp, c, timed):
     """The same dense attention through torch.nn.functional.scaled_dot_product_attention (the
     platform's flash-attention library), timing only: the KV heads are expanded to the query
@@ -357,6 +377,11 @@ def main():
         legs["recsa_prefill_last_chunk"] = {"ms_per_call": round(ms, 4), "tokens_per_call": w.B * c,
                                             "tokens_per_s": round(w.B * c / (ms * 1e-3), 1),
                                             "positions": [w.L - c, w.L]}
+        psw = R.recsa_sel_width(sh, w.L - c + 1, w.L, k)
+        psel = torch.empty(w.B, c, w.Hkv, len(k), psw, dtype=torch.int32, device=dev)
+        R.recsa_prefill(sh, qp, w.L - c, K, V, tree, k, pout, None, psel, psw, pws)
+        legs["recsa_prefill_last_chunk"]["tile_sharing"] = tile_sharing(psel.cpu().numpy())
+        del psel
         pmode = R.RECSA_DENSE_KEYS_ROTATED | R.RECSA_DENSE_CAUSAL
         dpws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, c, pmode), 16), dtype=torch.uint8, device=dev)
         ms = timed(lambda: R.recsa_dense_ref_attn(sh, qp, w.L - c, Kr, V, w.L, pmode, pout, None, dpws), 2)
