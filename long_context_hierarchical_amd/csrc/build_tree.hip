@@ -80,9 +80,19 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
   constexpr int T = Gm::T, CH = Gm::CH, NPW = Gm::NPW, NPT = Gm::NPT;
   constexpr int PF = BF16 ? 2 : 1;        // children per register batch
   static_assert(NPT == 2, "phase 2 tiles 4 outputs x 2 nodes per thread");
-  __shared__ float wt[D][D];              // wt[j][i] = W[i][j], float32
+  // bf16 storage keeps W as stored (bf16, exact) and stages the tile's node rows for the
+  // fused parents; float32 storage keeps W as float32 and re-reads the node rows
+  constexpr bool STAGE = BF16 && FUSE;
+  using WT = typename std::conditional<BF16, uint16_t, float>::type;
+  __shared__ WT wt[D][D];                 // wt[j][i] = W[i][j]
   __shared__ float mt[D][NPW];            // mt[j][node] = mean of the node's child keys
+  __shared__ uint16_t k1s[STAGE ? NPW : 1][D];   // the tile's node keys / values (bf16 bits)
+  __shared__ uint16_t v1s[STAGE ? NPW : 1][D];
   float* const m2s = &mt[0][0];           // parents' key means [P][D] reuse mt after phase 2
+  auto wload = [&](int j, int i) -> float {
+    if constexpr (BF16) return bf16_to_f32(wt[j][i]);
+    else return wt[j][i];
+  };
 
   const int tid = threadIdx.x;
   const int f = a.f;
@@ -95,7 +105,10 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
     float x[8];
     load8<BF16>(a.W, static_cast<int64_t>(i) * D + j0, x);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) wt[j0 + e][i] = x[e];
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (BF16) wt[j0 + e][i] = static_cast<uint16_t>(__float_as_uint(x[e]) >> 16);
+      else wt[j0 + e][i] = x[e];
+    }
   }
 
   const float ff = static_cast<float>(f);
@@ -166,6 +179,17 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
         nv[e] = round_store<BF16>(div_f(sv[e]));
       }
       store8<BF16>(a.dstV, (bh * a.dst_rows + g) * D + ch * 8, nv);
+      if constexpr (STAGE) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v1s[nl][ch * 8 + e] = static_cast<uint16_t>(__float_as_uint(nv[e]) >> 16);
+      }
+    } else if (STAGE && g < a.g_lo) {
+      // a node built by an earlier call: its stored key and value feed the parent
+      const int64_t off = (bh * a.dst_rows + g) * D + ch * 8;
+      const uint4 xk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dstK) + off);
+      const uint4 xv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.dstV) + off);
+      *reinterpret_cast<uint4*>(&k1s[nl][ch * 8]) = xk;
+      *reinterpret_cast<uint4*>(&v1s[nl][ch * 8]) = xv;
     }
     __syncthreads();
     prefetch(tile + gridDim.x);
@@ -179,9 +203,16 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
       for (int o = 0; o < 4; ++o) acc[u][o] = 0.0f;
 #pragma unroll 8
     for (int j = 0; j < D; ++j) {
-      const float4 w4 = *reinterpret_cast<const float4*>(&wt[j][o0]);
+      float wv[4];
+      if constexpr (BF16) {
+        const uint2 w4 = *reinterpret_cast<const uint2*>(&wt[j][o0]);
+        wv[0] = __uint_as_float(w4.x << 16); wv[1] = __uint_as_float(w4.x & 0xFFFF0000u);
+        wv[2] = __uint_as_float(w4.y << 16); wv[3] = __uint_as_float(w4.y & 0xFFFF0000u);
+      } else {
+        const float4 w4 = *reinterpret_cast<const float4*>(&wt[j][o0]);
+        wv[0] = w4.x; wv[1] = w4.y; wv[2] = w4.z; wv[3] = w4.w;
+      }
       const float2 m2 = *reinterpret_cast<const float2*>(&mt[j][n0]);
-      const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
       const float mv[2] = {m2.x, m2.y};
 #pragma unroll
       for (int u = 0; u < NPT; ++u)
@@ -197,6 +228,8 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
           const uint32_t b0 = f32_to_bf16_bits(acc[u][0]), b1 = f32_to_bf16_bits(acc[u][1]);
           const uint32_t b2 = f32_to_bf16_bits(acc[u][2]), b3 = f32_to_bf16_bits(acc[u][3]);
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dstK) + off) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+          if constexpr (STAGE)
+            *reinterpret_cast<uint2*>(&k1s[n0 + u][o0]) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
         } else {
           *reinterpret_cast<float4*>(static_cast<float*>(a.dstK) + off) =
               make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
@@ -210,32 +243,45 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
       const int64_t p_lo = a.g_lo / f, p_hi = a.g_hi / f, pb = tb / f;
       if (pb + P > p_lo && pb < p_hi) {
         __syncthreads();   // the tile's node rows are stored and visible to the workgroup
-        for (int it = tid; it < P * 2 * CH; it += T) {
-          const int p = it / (2 * CH), rem = it % (2 * CH), which = rem / CH, cc = rem % CH;
-          const int64_t g2 = pb + p;
-          if (g2 < p_lo || g2 >= p_hi) continue;
-          const void* src = which ? a.dstV : a.dstK;
-          const int64_t rb = (bh * a.dst_rows + g2 * f) * D + cc * 8;
-          float s8[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s8[e] = 0.0f;
-          for (int c0 = 0; c0 < f; c0 += 4) {
-            Chunk<BF16> x[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (c0 + u < f) x[u].load(src, rb + static_cast<int64_t>(c0 + u) * D);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (c0 + u < f) x[u].add_to(s8);
+        if constexpr (STAGE) {
+          for (int it = tid; it < P * 2 * D; it += T) {
+            const int p = it / (2 * D), rem = it % (2 * D), which = rem / D, dd = rem % D;
+            const int64_t g2 = pb + p;
+            if (g2 < p_lo || g2 >= p_hi) continue;
+            const uint16_t(*src)[D] = which ? v1s : k1s;
+            float s1 = 0.0f;
+            for (int c = 0; c < f; ++c) s1 = s1 + bf16_to_f32(src[p * f + c][dd]);
+            if (which == 0) m2s[p * D + dd] = div_f(s1);
+            else store1<BF16>(a.dst2V, (bh * a.dst2_rows + g2) * D + dd, round_store<BF16>(div_f(s1)));
           }
-          if (which == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m2s[p * D + cc * 8 + e] = div_f(s8[e]);
-          } else {
-            float o8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o8[e] = round_store<BF16>(div_f(s8[e]));
-            store8<BF16>(a.dst2V, (bh * a.dst2_rows + g2) * D + cc * 8, o8);
+        } else {
+          for (int it = tid; it < P * 2 * CH; it += T) {
+            const int p = it / (2 * CH), rem = it % (2 * CH), which = rem / CH, cc = rem % CH;
+            const int64_t g2 = pb + p;
+            if (g2 < p_lo || g2 >= p_hi) continue;
+            const void* src = which ? a.dstV : a.dstK;
+            const int64_t rb = (bh * a.dst_rows + g2 * f) * D + cc * 8;
+            float s8[8];
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) s8[e] = 0.0f;
+            for (int c0 = 0; c0 < f; c0 += 4) {
+              Chunk<BF16> x[4];
+  #pragma unroll
+              for (int u = 0; u < 4; ++u)
+                if (c0 + u < f) x[u].load(src, rb + static_cast<int64_t>(c0 + u) * D);
+  #pragma unroll
+              for (int u = 0; u < 4; ++u)
+                if (c0 + u < f) x[u].add_to(s8);
+            }
+            if (which == 0) {
+  #pragma unroll
+              for (int e = 0; e < 8; ++e) m2s[p * D + cc * 8 + e] = div_f(s8[e]);
+            } else {
+              float o8[8];
+  #pragma unroll
+              for (int e = 0; e < 8; ++e) o8[e] = round_store<BF16>(div_f(s8[e]));
+              store8<BF16>(a.dst2V, (bh * a.dst2_rows + g2) * D + cc * 8, o8);
+            }
           }
         }
         __syncthreads();
@@ -245,7 +291,7 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
           if (g2 < p_lo || g2 >= p_hi) continue;
           float acc2 = 0.0f;
 #pragma unroll 8
-          for (int j = 0; j < D; ++j) acc2 = fmaf(wt[j][i], m2s[p * D + j], acc2);
+          for (int j = 0; j < D; ++j) acc2 = fmaf(wload(j, i), m2s[p * D + j], acc2);
           store1<BF16>(a.dst2K, (bh * a.dst2_rows + g2) * D + i, round_store<BF16>(acc2));
         }
       }

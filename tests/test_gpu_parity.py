@@ -50,7 +50,7 @@ BUILD_CASES = [
     _w("b_bf16_d128_f32", Hq=4, Hkv=1, d=128, dtype="bf16", L=32 ** 2 * 5 + 31, f=32, seed=3),
     _w("b_f32_d64_f3", L=3 ** 7 + 5, f=3, seed=4),
     _w("b_bf16_d64_f5", B=2, Hq=2, Hkv=2, d=64, dtype="bf16", L=5 ** 5 + 9, f=5, seed=5),
-    # fanout equal to the pool kernel's tile (d=128: 16, d=64: 32): level pairs built in one pass
+    # fanouts dividing the pool kernel's tile (d=128: 32 nodes, d=64: 64): level pairs built in one pass
     _w("b_bf16_d64_f32_fused", Hq=2, Hkv=1, d=64, dtype="bf16", L=32 ** 3 + 32 * 7 + 5, f=32, seed=7),
     _w("b_f32_d64_f32_fused", Hq=2, Hkv=2, d=64, dtype="f32", L=32 ** 2 * 3 + 40, f=32, seed=8),
     _w("b_bf16_d128_f16_deep", Hq=8, Hkv=2, d=128, dtype="bf16", L=16 ** 4 + 16 ** 2 * 5 + 3, f=16, seed=9),
