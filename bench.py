@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=24, help="oracle decode units timed for the baseline")
     ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--no-step-mode", action="store_true", help="skip timing one-query-per-sequence decode calls")
+    ap.add_argument("--no-hbm-probe", action="store_true",
+                    help="skip measuring the achievable HBM read/copy bandwidth with the probe program")
     ap.add_argument("--no-library-legs", action="store_true",
                     help="skip the library flash-attention comparison (torch scaled_dot_product_attention)")
     ap.add_argument("--no-legs", action="store_true", help="skip the dense and prefill comparison legs")
@@ -46,6 +48,22 @@ def parse():
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def hbm_probe():
+    """Achievable HBM read and copy bandwidth on this GPU from the probe program built with the
+    library (streaming kernels over 8 GiB), or the reason it could not run."""
+    import subprocess
+    exe = os.path.join(ROOT, "long_context_hierarchical_amd", "probe", "hbm_probe")
+    if not os.path.exists(exe):
+        return {"error": "probe program not built"}
+    try:
+        r = subprocess.run([exe, "8"], capture_output=True, text=True, timeout=120)
+    except subprocess.TimeoutExpired:
+        return {"error": "probe timed out"}
+    if r.returncode != 0:
+        return {"error": (r.stderr or r.stdout).strip()[-200:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def kernel_hash(*names):
@@ -223,6 +241,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    # run first, as a child process, before this process touches the GPU
+    probe = None if args.no_hbm_probe else hbm_probe()
+
     import numpy as np
     import torch
 
@@ -301,9 +322,13 @@ def main():
     def roof(name):
         ki = kinfo[name]
         ach = ki["bytes"] / (ki["ms"] * 1e-3) / 1e9
-        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(name, ki["src"]),
-                "kernel": name}
+        r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(name, ki["src"]),
+             "kernel": name}
+        if probe and "read_GBps" in probe:
+            r["measured_read_peak"] = probe["read_GBps"]
+            r["frac_of_measured_read"] = round(ach / probe["read_GBps"], 4)
+        return r
 
     res = {
         "metric": METRIC,
@@ -330,6 +355,7 @@ def main():
             "decode_bytes_per_query": qb_bytes, "decode_rows_per_unit": rows,
             "build_bytes": bb, "tree_nodes_per_slice": n_nodes,
             "roofline_other": roof("attend_kernel" if dom == "pool_kernel" else "pool_kernel"),
+            "hbm_probe": probe,
         },
     }
 

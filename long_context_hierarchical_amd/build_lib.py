@@ -11,6 +11,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "librecsa.so")
 SOURCES = ["build_tree.hip", "attend.hip", "dense.hip", "api.cpp"]
+# HBM read/copy probe (a separate program, not part of the library): the achievable bandwidth
+PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
+PROBE = os.path.join(PKG, "probe", "hbm_probe")
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -49,6 +52,12 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, OUT)
+    cmd = [cc, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", PROBE_SRC, "-o", PROBE + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(PROBE + ".tmp", PROBE)
     return OUT
 
 
