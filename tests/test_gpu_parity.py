@@ -184,6 +184,36 @@ def test_decode_launch_shapes_agree_bitwise():
         assert np.array_equal(one[1][:, 0].view(np.uint32), big[1][:, j].view(np.uint32)), j
 
 
+ONE_WAVE_CASES = [
+    # (workload with >= 2048 (sequence, query, KV head) units per call, k per level)
+    (_w("w1_f32_d64_G1_f3", Hq=2, Hkv=2, d=64, dtype="f32", L=1000, f=3, k=2, n_queries=1100, seed=41),
+     [2, 3, 1, 2, 2, 4]),
+    (_w("w1_bf16_d64_G2_f4", B=2, Hq=4, Hkv=2, d=64, dtype="bf16", L=777, f=4, k=3, n_queries=520, seed=42),
+     [0, 3, 1, 5]),
+    (_w("w1_bf16_d128_G8_f32", Hq=16, Hkv=2, d=128, dtype="bf16", L=40000, f=32, k=16, n_queries=1030, seed=43),
+     [16] * 3),
+    (_w("w1_f32_d128_G4_f16", Hq=8, Hkv=2, d=128, dtype="f32", L=5000, k=8, n_queries=1030, seed=44), [8] * 3),
+]
+
+
+@pytest.mark.parametrize("w,k", ONE_WAVE_CASES, ids=lambda x: getattr(x, "name", ""))
+def test_decode_one_wave_per_unit_variants(w, k):
+    """Calls large enough for one wave per unit, for each storage type, head size and group
+    size: sampled units against the oracle, and every sampled query bitwise equal to the same
+    query decoded alone (several waves per unit)."""
+    _say(f"decode one-wave {w.name}")
+    inp = gen_decode_inputs(w)
+    g = Gpu(w, inp)
+    big = g.decode(k, w.L)
+    js = [0, 1, w.n_queries // 2, w.n_queries - 1]
+    units = [(b, j, h) for b in range(w.B) for j in js for h in range(w.Hkv)]
+    _check_units(w, inp, big, k, units, "decode", n_tokens=w.L)
+    for j in js:
+        one = g.decode(k, w.L, q=g.q[:, j:j + 1].contiguous())
+        assert np.array_equal(one[2][:, 0], big[2][:, j]), j
+        assert np.array_equal(one[0][:, 0].view(np.uint32), big[0][:, j].view(np.uint32)), j
+
+
 # ------------------------------------------------------------------ prefill
 
 def test_prefill_matches_oracle_and_chunking():
