@@ -60,6 +60,44 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Sum over each group of N (4 or 8) consecutive lanes, left in every lane of the group, with
+// DPP lane moves (no LDS round trip): pairs of lanes, pairs of pairs, then (N = 8) the two
+// quads of the half-row, mirrored.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(N == 4 || N == 8, "groups of 4 or 8 lanes");
+  x = x + dpp_move<0xB1>(x);                          // quad_perm [1, 0, 3, 2]
+  x = x + dpp_move<0x4E>(x);                          // quad_perm [2, 3, 0, 1]
+  if constexpr (N == 8) x = x + dpp_move<0x141>(x);   // row_half_mirror
+  return x;
+}
+
+// Wave-wide sum / max with DPP inside each 16-lane row (pairs, quads, half-rows, rows), then
+// the four row results combined in a fixed order from lanes 0, 16, 32 and 48; every lane
+// gets the same value.
+__device__ __forceinline__ float lane_read(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x = x + dpp_move<0xB1>(x);
+  x = x + dpp_move<0x4E>(x);
+  x = x + dpp_move<0x141>(x);   // row_half_mirror
+  x = x + dpp_move<0x140>(x);   // row_mirror
+  return (lane_read(x, 0) + lane_read(x, 16)) + (lane_read(x, 32) + lane_read(x, 48));
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_move<0xB1>(x));
+  x = fmaxf(x, dpp_move<0x4E>(x));
+  x = fmaxf(x, dpp_move<0x141>(x));
+  x = fmaxf(x, dpp_move<0x140>(x));
+  return fmaxf(fmaxf(lane_read(x, 0), lane_read(x, 16)), fmaxf(lane_read(x, 32), lane_read(x, 48)));
+}
+
 // 4 consecutive storage elements -> float.
 template <bool BF16>
 __device__ __forceinline__ void load4(const void* base, int64_t off, float (&x)[4]) {
@@ -390,37 +428,38 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
     bsync();
   };
 
-  // logits of candidates [c0, c0 + cn) (index = RoPE position) -> zs[hh * zcap + r], sc[r]
-  // The rows of the next pass are loaded before the current pass is computed.
-  auto score_rows = [&](const void* src, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn) {
+  // logits of candidates [c0, c0 + cn) (index = RoPE position) -> zs[hh * zcap + r], sc[r].
+  // Two row buffers alternate: the rows of the next pass are requested after this pass's
+  // RoPE-table entries, so waiting for the table does not wait for them. The loop body has
+  // no branch around a load (the rotation is chosen outside the loop; a pass past the end
+  // and lanes past the last candidate load the last candidate's row and write nothing), so
+  // the loads' completion is tracked exactly.
+  auto score_rows_t = [&](const void* src, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn, auto rope) {
+    constexpr bool ROPE = decltype(rope)::value;
     auto fetch = [&](int32_t r0, Raw8<BF16>& lo, Raw8<BF16>& hi) {
-      const int32_t r = r0 + srg;
-      if (r < cn) {
-        const int64_t off = (rowbase + cm(c0 + r)) * D + 8 * ssub;
-        lo = raw8_load<BF16>(src, off);
-        hi = raw8_load<BF16>(src, off + HALF);
-      } else {
-        lo = raw8_zero<BF16>();
-        hi = raw8_zero<BF16>();
-      }
+      const int32_t r = r0 + srg < cn ? r0 + srg : cn - 1;
+      const int64_t off = (rowbase + cm(c0 + r)) * D + 8 * ssub;
+      lo = raw8_load<BF16>(src, off);
+      hi = raw8_load<BF16>(src, off + HALF);
     };
-    Raw8<BF16> nlo, nhi;
-    fetch(wid * SPP, nlo, nhi);
-    for (int32_t r0 = wid * SPP; r0 < cn; r0 += NW * SPP) {
+    auto pass = [&](int32_t r0, const Raw8<BF16>& clo, const Raw8<BF16>& chi, Raw8<BF16>& nlo, Raw8<BF16>& nhi) {
       const int32_t r = r0 + srg;
       const bool valid = r < cn;
-      const int32_t i = c0 + r;
+      float4 tv[4];
+      if constexpr (ROPE) {
+        const float4* t = reinterpret_cast<const float4*>(a.tab + static_cast<int64_t>(c0 + (valid ? r : 0)) * HALF + 8 * ssub);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tv[u] = t[u];
+      }
+      fetch(r0 + NW * SPP, nlo, nhi);
       float klo[8], khi[8];
-      raw8_cvt<BF16>(nlo, klo);
-      raw8_cvt<BF16>(nhi, khi);
-      if (r0 + NW * SPP < cn) fetch(r0 + NW * SPP, nlo, nhi);
+      raw8_cvt<BF16>(clo, klo);
+      raw8_cvt<BF16>(chi, khi);
       float olo[8], ohi[8];
-      if (a.use_rope) {
-        const float4* t = reinterpret_cast<const float4*>(a.tab + static_cast<int64_t>(valid ? i : 0) * HALF + 8 * ssub);
+      if constexpr (ROPE) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float4 tv = t[u];
-          const float cc[2] = {tv.x, tv.z}, ss[2] = {tv.y, tv.w};
+          const float cc[2] = {tv[u].x, tv[u].z}, ss[2] = {tv[u].y, tv[u].w};
 #pragma unroll
           for (int v = 0; v < 2; ++v) {
             const int e = 2 * u + v;
@@ -466,9 +505,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
         }
       }
 #pragma unroll
-      for (int off = SL / 2; off >= 1; off >>= 1)
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) part[hh] += __shfl_xor(part[hh], off);
+      for (int hh = 0; hh < G; ++hh) part[hh] = lane_group_sum<SL>(part[hh]);
       if (valid && ssub == 0) {
         float S = 0.0f;
 #pragma unroll
@@ -479,10 +516,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
         }
         sc[r] = S;
       }
+    };
+    Raw8<BF16> alo, ahi, blo, bhi;
+    int32_t r0 = wid * SPP;
+    fetch(r0, alo, ahi);
+    for (; r0 < cn; r0 += 2 * NW * SPP) {
+      pass(r0, alo, ahi, blo, bhi);
+      if (r0 + NW * SPP >= cn) break;
+      pass(r0 + NW * SPP, blo, bhi, alo, ahi);
     }
     bsync();
   };
-
+  auto score_rows = [&](const void* src, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn) {
+    if (a.use_rope) score_rows_t(src, rowbase, cm, c0, cn, std::true_type{});
+    else score_rows_t(src, rowbase, cm, c0, cn, std::false_type{});
+  };
   // Keeps the s largest (S, -r) keys among r < C: flags[r] = 1 and sel_out[0..s) = their
   // node ids in candidate order. The s-th largest score is found by bisection on its
   // order-preserving 32-bit pattern (a ballot count per step, no lane exchange); the
@@ -553,7 +601,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
         for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(mnew[hh], zs[hh * zcap + r]);
       }
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(m_run[hh], wave_max(mnew[hh]));
+      for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(m_run[hh], wave_max_dpp(mnew[hh]));
       float ls[G];
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) ls[hh] = 0.0f;
@@ -568,7 +616,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const float lsum = wave_sum(ls[hh]);
+        const float lsum = wave_sum_dpp(ls[hh]);
         const float alpha = expf(m_run[hh] - mnew[hh]);
         l_run[hh] = l_run[hh] * alpha + lsum;
         m_run[hh] = mnew[hh];
