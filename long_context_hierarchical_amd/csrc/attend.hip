@@ -300,7 +300,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
   constexpr int SL = D / 16;           // lanes per row, score phase (8 rotate-half pairs per lane)
   constexpr int SPP = kWave / SL;      // rows per pass, score phase
   constexpr int HALF = D / 2;
-  constexpr int PV_UNROLL = NW == 1 ? 4 : 16;
+  constexpr int PV_UNROLL = NW == 1 ? 4 : 8;
   static_assert(VE % NW == 0, "waves split the value elements of a lane");
 
   extern __shared__ __align__(16) unsigned char lds[];
@@ -642,22 +642,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
         }
       }
     }
-    for (int32_t r0 = 0; r0 < cn; r0 += RPP * PV_UNROLL) {
-      RawV<BF16, VEW> raw[PV_UNROLL];
-      bool live[PV_UNROLL];
+    // value rows: two buffers alternate, the next iteration's rows are requested before this
+    // iteration's are accumulated; every row slot loads (a kept or absent row loads a valid
+    // row and adds nothing), so no load sits behind a branch
+    auto vfetch = [&](int32_t r0, RawV<BF16, VEW> (&raw)[PV_UNROLL]) {
 #pragma unroll
       for (int u = 0; u < PV_UNROLL; ++u) {
         const int32_t r = r0 + u * RPP + rg;
-        live[u] = r < cn && !(use_flags && flags[r]);
-        if (live[u]) raw[u].load(vsrc, (rowbase + cm(c0 + r)) * D + dim0);
-        else raw[u].zero();
+        raw[u].load(vsrc, (rowbase + cm(c0 + (r < cn ? r : cn - 1))) * D + dim0);
       }
+    };
+    auto vpass = [&](int32_t r0, const RawV<BF16, VEW> (&cur)[PV_UNROLL], RawV<BF16, VEW> (&nxt)[PV_UNROLL]) {
+      vfetch(r0 + RPP * PV_UNROLL, nxt);
 #pragma unroll
       for (int u = 0; u < PV_UNROLL; ++u) {
-        if (!live[u]) continue;
-        float v[VEW];
-        raw[u].cvt(v);
         const int32_t r = r0 + u * RPP + rg;
+        if (r >= cn || (use_flags && flags[r])) continue;
+        float v[VEW];
+        cur[u].cvt(v);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
           const float p = zs[hh * zcap + r];
@@ -665,6 +667,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
           for (int e = 0; e < VEW; ++e) acc[hh][e] = fmaf(p, v[e], acc[hh][e]);
         }
       }
+    };
+    RawV<BF16, VEW> va[PV_UNROLL], vb[PV_UNROLL];
+    vfetch(0, va);
+    for (int32_t r0 = 0; r0 < cn; r0 += 2 * RPP * PV_UNROLL) {
+      vpass(r0, va, vb);
+      if (r0 + RPP * PV_UNROLL >= cn) break;
+      vpass(r0 + RPP * PV_UNROLL, vb, va);
     }
     bsync();
   };
