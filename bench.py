@@ -328,6 +328,10 @@ def main():
         if probe and "read_GBps" in probe:
             r["measured_read_peak"] = probe["read_GBps"]
             r["frac_of_measured_read"] = round(ach / probe["read_GBps"], 4)
+        if name == "pool_kernel" and probe and "read16_write1_GBps" in probe:
+            # the build reads every child row once and writes one node row per f rows read
+            r["measured_mix_peak"] = probe["read16_write1_GBps"]
+            r["frac_of_measured_mix"] = round(ach / probe["read16_write1_GBps"], 4)
         return r
 
     res = {

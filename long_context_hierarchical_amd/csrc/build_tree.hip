@@ -23,6 +23,15 @@
 
 namespace recsa {
 
+// Workgroup barrier that orders LDS only: the waves' outstanding global loads (the next
+// tile's prefetch) and stores stay in flight across it, where __syncthreads() would wait for
+// all of them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <bool BF16>
 struct Chunk;  // raw storage of 8 consecutive elements
 template <>
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
     }
   };
   prefetch(blockIdx.x);
-  __syncthreads();
+  lds_barrier();
 
   for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int64_t bh = tile / tiles_per_bh;
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
       *reinterpret_cast<uint4*>(&k1s[nl][ch * 8]) = xk;
       *reinterpret_cast<uint4*>(&v1s[nl][ch * 8]) = xv;
     }
-    __syncthreads();
+    lds_barrier();
     prefetch(tile + gridDim.x);
 
     // phase 2: key_i = sum_j W[i][j] m_j, accumulated in input order j = 0..D-1, one
@@ -242,7 +251,8 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
       const int P = NPW / f;
       const int64_t p_lo = a.g_lo / f, p_hi = a.g_hi / f, pb = tb / f;
       if (pb + P > p_lo && pb < p_hi) {
-        __syncthreads();   // the tile's node rows are stored and visible to the workgroup
+        if constexpr (STAGE) lds_barrier();   // the tile's node rows are in LDS
+        else __syncthreads();                 // the tile's node rows are stored and visible
         if constexpr (STAGE) {
           for (int it = tid; it < P * 2 * D; it += T) {
             const int p = it / (2 * D), rem = it % (2 * D), which = rem / D, dd = rem % D;
@@ -284,7 +294,7 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
             }
           }
         }
-        __syncthreads();
+        lds_barrier();
         for (int it = tid; it < P * D; it += T) {
           const int p = it / D, i = it % D;
           const int64_t g2 = pb + p;
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
