@@ -434,7 +434,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
   // no branch around a load (the rotation is chosen outside the loop; a pass past the end
   // and lanes past the last candidate load the last candidate's row and write nothing), so
   // the loads' completion is tracked exactly.
-  auto score_rows_t = [&](const void* src, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn, auto rope) {
+  auto score_rows_t = [&](const void* src, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn, int64_t qpos,
+                          auto rope) {
     constexpr bool ROPE = decltype(rope)::value;
     auto fetch = [&](int32_t r0, Raw8<BF16>& lo, Raw8<BF16>& hi) {
       const int32_t r = r0 + srg < cn ? r0 + srg : cn - 1;
@@ -520,6 +521,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
     Raw8<BF16> alo, ahi, blo, bhi;
     int32_t r0 = wid * SPP;
     fetch(r0, alo, ahi);
+    if (qpos >= 0) rotate_query(qpos);   // its table reads overlap the first rows' loads
     for (; r0 < cn; r0 += 2 * NW * SPP) {
       pass(r0, alo, ahi, blo, bhi);
       if (r0 + NW * SPP >= cn) break;
@@ -527,9 +529,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
     }
     bsync();
   };
-  auto score_rows = [&](const void* src, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn) {
-    if (a.use_rope) score_rows_t(src, rowbase, cm, c0, cn, std::true_type{});
-    else score_rows_t(src, rowbase, cm, c0, cn, std::false_type{});
+  // qpos >= 0: rotate the query heads at qpos first (a level's first chunk)
+  auto score_rows = [&](const void* src, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn, int64_t qpos) {
+    if (a.use_rope) score_rows_t(src, rowbase, cm, c0, cn, qpos, std::true_type{});
+    else score_rows_t(src, rowbase, cm, c0, cn, qpos, std::false_type{});
   };
   // Keeps the s largest (S, -r) keys among r < C: flags[r] = 1 and sel_out[0..s) = their
   // node ids in candidate order. The s-th largest score is found by bisection on its
@@ -694,8 +697,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
       bsync();
     } else {
       const int64_t rowbase = bh * a.tree.rows[lv];
-      rotate_query(C);
-      score_rows(a.tree.NK[lv], rowbase, cm, 0, C);
+      score_rows(a.tree.NK[lv], rowbase, cm, 0, C, C);
       if (s > 0) {
         if (wid == 0) select_top(C, s, cm, sel_new);
       } else {
@@ -722,10 +724,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
     const bool own = a.prefill && C0 > 0 && cm(C0 - 1) == n - 1;
     const int32_t pq = own ? C0 - 1 : C0;
     const int64_t rowbase = bh * a.cap;
-    if (C0 > 0) rotate_query(pq);
     for (int64_t c0 = 0; c0 < C0; c0 += zcap) {
       const int32_t cn = static_cast<int32_t>(C0 - c0 < zcap ? C0 - c0 : zcap);
-      score_rows(a.K, rowbase, cm, static_cast<int32_t>(c0), cn);
+      score_rows(a.K, rowbase, cm, static_cast<int32_t>(c0), cn, c0 == 0 ? pq : -1);
       softmax_pv(a.V, rowbase, cm, static_cast<int32_t>(c0), cn, false);
     }
   }
