@@ -535,8 +535,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
     else score_rows_t(src, rowbase, cm, c0, cn, qpos, std::false_type{});
   };
   // Keeps the s largest (S, -r) keys among r < C: flags[r] = 1 and sel_out[0..s) = their
-  // node ids in candidate order. The s-th largest score is found by bisection on its
-  // order-preserving 32-bit pattern (a ballot count per step, no lane exchange); the
+  // node ids in candidate order. A threshold is found by bisection on the scores'
+  // order-preserving 32-bit patterns (a ballot count per step, no lane exchange); the
   // candidates above it are kept, then those equal to it in index order.
   auto select_top = [&](int32_t C, int32_t s, const CandMap& cm, int32_t* sel_out) {
     const int32_t nu = (C + kWave - 1) / kWave;
@@ -558,10 +558,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
       for (int u = 4; u < nu; ++u) c += __popcll(__ballot(key(u) >= t));
       return c;
     };
+    // tau: the largest t with at least s keys >= t; once exactly s keys are >= some t they
+    // are the selection (nothing left to tie-break), so the search stops there
     uint32_t tau = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t t = tau | (1u << bit);
-      if (count_ge(t) >= s) tau = t;
+      const int32_t c = count_ge(t);
+      if (c >= s) {
+        tau = t;
+        if (c == s) break;
+      }
     }
     int32_t above = 0;
 #pragma unroll
