@@ -130,6 +130,17 @@ def pool_launches(w):
     return (T + 1) // 2 if fused else T
 
 
+def decode_alu(w, rows, n_queries, decode_ms):
+    """The decode kernel against the vector-ALU roofline (it is issue-bound, its row reads
+    mostly hit the cache): algorithmic flops 2 * d * H_q * (scored rows + softmax entries) per
+    query, i.e. one multiply-add per (query head, element) for every logit and every weighted
+    value row; key rotation, selection and exponentials are not counted."""
+    per_query = 2 * w.d * w.Hq * (rows["key_rows"] + rows["tok_rows"] + rows["val_rows"] + rows["tok_rows"])
+    ach = per_query * n_queries / (decode_ms * 1e-3) / 1e12
+    return {"bound": "alu", "achieved": round(ach, 2), "peak": 157.3, "unit": "TFLOP/s",
+            "frac": round(ach / 157.3, 4), "flops_per_query": per_query}
+
+
 def tile_sharing(sel):
     """How many (query, KV head) units of one call share each candidate tile: at level l the
     children of the level-(l+1) node kept at rank r form one tile of keys rotated at the same
@@ -359,6 +370,7 @@ def main():
             "decode_bytes_per_query": qb_bytes, "decode_rows_per_unit": rows,
             "build_bytes": bb, "tree_nodes_per_slice": n_nodes,
             "roofline_other": roof("attend_kernel" if dom == "pool_kernel" else "pool_kernel"),
+            "decode_alu": decode_alu(w, rows, n_queries, decode_ms),
             "hbm_probe": probe,
         },
     }
