@@ -43,6 +43,9 @@ def parse():
                     help="skip the library flash-attention comparison (torch scaled_dot_product_attention)")
     ap.add_argument("--no-legs", action="store_true", help="skip the dense and prefill comparison legs")
     ap.add_argument("--prefill-chunk", type=int, default=4096)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step benchmark, sweep the context length (decode 4K-2M, chunked "
+                         "prefill 4K-64K) at the 131K workload's shape and print one JSON line of it")
     return ap.parse_args()
 
 
@@ -128,6 +131,105 @@ def pool_launches(w):
         m //= w.f
     fused = {128: 32, 64: 64}[w.d] % w.f == 0
     return (T + 1) // 2 if fused else T
+
+
+def sweep():
+    """Context-length sweep at the 131K workload's shape (one sequence, 32 query heads, 8 KV
+    heads, d = 128, bf16, f = 16, k = 8): for L = 4K..2M (powers of 2) the full tree build, a
+    256-query batched decode, a 1-query decode step and the dense 1-query decode step; for
+    L = 4K..64K the causal prefill of all L positions in chunks of 4096 (the tree extended
+    chunk by chunk) against dense causal prefill. Seeded random inputs, timing only."""
+    import torch
+
+    from long_context_hierarchical_amd import recsa as R
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, d, f, kk, nq = 1, 32, 8, 128, 16, 8, 256
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2024)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def inputs(L, n_q):
+        s = d ** -0.5
+        K = (torch.randn(B, Hkv, L, d, device=dev, generator=gen) * s).to(torch.bfloat16)
+        V = (torch.randn(B, Hkv, L, d, device=dev, generator=gen) * s).to(torch.bfloat16)
+        q = (torch.randn(B, n_q, Hq, d, device=dev, generator=gen) * s).to(torch.bfloat16)
+        W = (torch.eye(d, device=dev) + 0.05 * s * torch.randn(d, d, device=dev, generator=gen)).to(torch.bfloat16)
+        return K, V, q, W
+
+    decode_rows = []
+    for lg in range(12, 22):
+        L = 1 << lg
+        log(f"sweep decode L={L}")
+        sh = R.Shape(B, Hkv, Hq, d, f, "bf16", L, 0.0, 1.0e6)
+        K, V, q, W = inputs(L, nq)
+        tree = torch.zeros(R.recsa_tree_bytes(sh), dtype=torch.uint8, device=dev)
+        T = R.recsa_num_levels(L, f)
+        k = [kk] * T
+        ws = torch.zeros(max(R.recsa_workspace_bytes(sh, L, k), 16), dtype=torch.uint8, device=dev)
+        out = torch.empty(B, nq, Hq, d, dtype=torch.float32, device=dev)
+        t_build = timed(lambda: R.recsa_build_tree(sh, K, V, W, 0, L, tree), 5)
+        t_dec = timed(lambda: R.recsa_decode(sh, q, K, V, tree, L, k, out, None, None, 0, ws), 10)
+        q1 = q[:, :1].contiguous()
+        o1 = torch.empty(B, 1, Hq, d, dtype=torch.float32, device=dev)
+        t_step = timed(lambda: R.recsa_decode(sh, q1, K, V, tree, L, k, o1, None, None, 0, ws), 20)
+        Kr = torch.empty_like(K)
+        R.recsa_rotate_keys(sh, K, L, Kr)
+        mode = R.RECSA_DENSE_KEYS_ROTATED
+        dws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, L, 1, mode), 16), dtype=torch.uint8, device=dev)
+        t_dense = timed(lambda: R.recsa_dense_ref_attn(sh, q1, 0, Kr, V, L, mode, o1, None, dws), 10)
+        nodes, m = 0, L // f
+        while m >= 1:
+            nodes += m
+            m //= f
+        build_bytes = B * Hkv * d * 2 * (2 * L + 2 * nodes)
+        decode_rows.append({"L": L, "levels": T, "build_ms": round(t_build, 4),
+                            "build_GBps": round(build_bytes / (t_build * 1e-3) / 1e9, 1),
+                            "decode_batched_ms": round(t_dec, 4),
+                            "decode_queries_per_s": round(B * nq / (t_dec * 1e-3), 1),
+                            "decode_step_ms": round(t_step, 4), "dense_step_ms": round(t_dense, 4),
+                            "step_speedup_vs_dense": round(t_dense / t_step, 2)})
+        del K, V, q, tree, Kr, dws, ws
+        torch.cuda.empty_cache()
+
+    prefill_rows = []
+    chunk = 4096
+    for lg in range(12, 17):
+        L = 1 << lg
+        log(f"sweep prefill L={L}")
+        sh = R.Shape(B, Hkv, Hq, d, f, "bf16", L, 0.0, 1.0e6)
+        K, V, q, W = inputs(L, L)
+        tree = torch.zeros(R.recsa_tree_bytes(sh), dtype=torch.uint8, device=dev)
+        k = [kk] * max(R.recsa_num_levels(L, f), 1)
+        ws = torch.zeros(max(R.recsa_workspace_bytes(sh, L, k), 16), dtype=torch.uint8, device=dev)
+        out = torch.empty(B, L, Hq, d, dtype=torch.float32, device=dev)
+
+        def recsa_prefill_all():
+            for c0 in range(0, L, chunk):
+                R.recsa_build_tree(sh, K, V, W, c0, c0 + chunk, tree)
+                R.recsa_prefill(sh, q[:, c0:c0 + chunk], c0, K, V, tree, k, out[:, c0:c0 + chunk], None, None, 0,
+                                ws)
+        t_r = timed(recsa_prefill_all, 2)
+        mode = R.RECSA_DENSE_CAUSAL
+        dws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, L, L, mode), 16), dtype=torch.uint8, device=dev)
+        t_d = timed(lambda: R.recsa_dense_ref_attn(sh, q, 0, K, V, L, mode, out, None, dws), 1)
+        prefill_rows.append({"L": L, "recsa_ms": round(t_r, 3), "recsa_tokens_per_s": round(L / (t_r * 1e-3), 1),
+                             "dense_ms": round(t_d, 3), "dense_tokens_per_s": round(L / (t_d * 1e-3), 1),
+                             "speedup": round(t_d / t_r, 2)})
+        del K, V, q, tree, out, dws, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "context length, 131K workload shape (B=1, Hq=32, Hkv=8, d=128, bf16, f=16, k=8)",
+                      "data": "synthetic (seeded random, timing only)",
+                      "decode": decode_rows, "prefill_chunked_4096": prefill_rows}), flush=True)
 
 
 def decode_alu(w, rows, n_queries, decode_ms):
@@ -251,6 +353,10 @@ def main():
               f"(the path shards by (sequence, KV head) with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep()
+        return
 
     # run first, as a child process, before this process touches the GPU
     probe = None if args.no_hbm_probe else hbm_probe()
