@@ -191,7 +191,10 @@ int32_t run_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, const
   if (bd.smax > kMaxList || bd.csel > kMaxList)
     return fail(RECSA_ERR_UNSUPPORTED, "candidate lists up to %lld entries exceed %lld", (long long)std::max(bd.smax, bd.csel),
                 (long long)kMaxList);
-  const int zcap = static_cast<int>(std::max<int64_t>(256, bd.csel));
+  // scored-candidate buffers: every selecting level fits whole; the token level is processed in
+  // chunks of zcap candidates, so an unbounded token list (no pruning) takes chunks of 256
+  const int64_t zneed = std::max<int64_t>(bd.csel, std::min<int64_t>(bd.c0, 256));
+  const int zcap = static_cast<int>((zneed + 15) / 16 * 16);
   const size_t lds = recsa::attend_lds_bytes(static_cast<int>(I.d), static_cast<int>(I.G), static_cast<int>(bd.smax),
                                              zcap);
   if (lds > kMaxLds) return fail(RECSA_ERR_UNSUPPORTED, "needs %zu bytes of LDS (max %zu)", lds, kMaxLds);

@@ -114,7 +114,7 @@ __device__ __forceinline__ void load4(const void* base, int64_t off, float (&x)[
 }
 
 struct Lds {
-  uint32_t q, qr, zs, sc, flags, selA, selB, nls, bc, total;
+  uint32_t q, qr, zs, sc, cid, flags, selA, selB, nls, bc, total;
 };
 
 __host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
@@ -126,6 +126,7 @@ __host__ __device__ inline Lds lds_layout(int d, int G, int smax, int zcap) {
   L.qr = o;    o = align16(o + 4u * G * d);         // rotated query operands of the current level
   L.zs = o;    o = align16(o + 4u * G * zcap);      // logits, then softmax weights, [G][zcap]
   L.sc = o;    o = align16(o + 4u * zcap);          // group scores
+  L.cid = o;   o = align16(o + 4u * zcap);          // node (or token) id of each scored candidate
   L.flags = o; o = align16(o + zcap);               // kept flags
   L.selA = o;  o = align16(o + 4u * smax);          // kept node ids, two buffers
   L.selB = o;  o = align16(o + 4u * smax);
@@ -312,6 +313,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
   uint32_t* qr = reinterpret_cast<uint32_t*>(lds + L.qr);
   float* zs = reinterpret_cast<float*>(lds + L.zs);
   float* sc = reinterpret_cast<float*>(lds + L.sc);
+  int32_t* cid = reinterpret_cast<int32_t*>(lds + L.cid);
   uint8_t* flags = reinterpret_cast<uint8_t*>(lds + L.flags);
   int32_t* selA = reinterpret_cast<int32_t*>(lds + L.selA);
   int32_t* selB = reinterpret_cast<int32_t*>(lds + L.selB);
@@ -439,7 +441,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
     constexpr bool ROPE = decltype(rope)::value;
     auto fetch = [&](int32_t r0, Raw8<BF16>& lo, Raw8<BF16>& hi) {
       const int32_t r = r0 + srg < cn ? r0 + srg : cn - 1;
-      const int64_t off = (rowbase + cm(c0 + r)) * D + 8 * ssub;
+      const int64_t off = (rowbase + cid[r]) * D + 8 * ssub;
       lo = raw8_load<BF16>(src, off);
       hi = raw8_load<BF16>(src, off + HALF);
     };
@@ -518,6 +520,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
         sc[r] = S;
       }
     };
+    // the chunk's candidate -> row map, read by the row loads, the selection and the values
+    for (int32_t r = tid; r < cn; r += NT) cid[r] = cm(c0 + r);
+    bsync();
     Raw8<BF16> alo, ahi, blo, bhi;
     int32_t r0 = wid * SPP;
     fetch(r0, alo, ahi);
@@ -538,7 +543,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
   // node ids in candidate order. A threshold is found by bisection on the scores'
   // order-preserving 32-bit patterns (a ballot count per step, no lane exchange); the
   // candidates above it are kept, then those equal to it in index order.
-  auto select_top = [&](int32_t C, int32_t s, const CandMap& cm, int32_t* sel_out) {
+  auto select_top = [&](int32_t C, int32_t s, int32_t* sel_out) {
     const int32_t nu = (C + kWave - 1) / kWave;
     uint32_t o[4];
 #pragma unroll
@@ -583,7 +588,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
       const bool keep = valid && (kv > tau || (kv == tau && taken + __popcll(eq & lt) < need));
       const uint64_t km = __ballot(keep);
       if (valid) flags[r] = keep ? 1 : 0;
-      if (keep) sel_out[cnt + __popcll(km & lt)] = cm(r);
+      if (keep) sel_out[cnt + __popcll(km & lt)] = cid[r];
       taken += __popcll(eq);
       cnt += __popcll(km);
     };
@@ -658,7 +663,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
 #pragma unroll
       for (int u = 0; u < PV_UNROLL; ++u) {
         const int32_t r = r0 + u * RPP + rg;
-        raw[u].load(vsrc, (rowbase + cm(c0 + (r < cn ? r : cn - 1))) * D + dim0);
+        raw[u].load(vsrc, (rowbase + cid[r < cn ? r : cn - 1]) * D + dim0);
       }
     };
     auto vpass = [&](int32_t r0, const RawV<BF16, VEW> (&cur)[PV_UNROLL], RawV<BF16, VEW> (&nxt)[PV_UNROLL]) {
@@ -705,7 +710,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
       const int64_t rowbase = bh * a.tree.rows[lv];
       score_rows(a.tree.NK[lv], rowbase, cm, 0, C, C);
       if (s > 0) {
-        if (wid == 0) select_top(C, s, cm, sel_new);
+        if (wid == 0) select_top(C, s, sel_new);
       } else {
         for (int32_t r = tid; r < C; r += NT) flags[r] = 0;
       }
