@@ -293,7 +293,11 @@ struct RawV {
 // chains as one wave, so every output element is accumulated in exactly the same order and
 // the results are bitwise those of NW = 1.
 template <int D, bool BF16, int G, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void attend_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void attend_kernel(AttnArgs args) {
+  // read the arguments in place: the per-level tables are indexed by a run-time level, and a
+  // by-value copy of the struct would be placed in scratch memory
+  (void)args;
+  const AttnArgs& a = *(const AttnArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
   constexpr int VE = 4;                // elements per row group lane (one wave), value phase
   constexpr int VEW = VE / NW;         // elements per lane of each wave
   constexpr int RL = D / VE;           // lanes per row, value phase
