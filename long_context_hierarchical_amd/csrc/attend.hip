@@ -27,15 +27,18 @@
 // token is one of them (causal prefill).
 //
 // A unit is a dependent chain of T + 1 rounds, so the kernel runs one wave per
-// unit with no workgroup barrier and lets many independent units share a CU.
+// unit with no workgroup barrier and lets many independent units share a CU;
+// calls with few units give each unit four waves instead (same arithmetic).
 // Lane layout: in the score phase D/16 lanes per candidate row, a lane holding
 // elements [8s, 8s+8) and their rotate-half partners [D/2 + 8s, ...), so the
-// rotation needs no lane exchange and the per-row reduction is 3 (d=128)
-// shuffle steps; bf16 operands are rounded and packed by v_cvt_pk_bf16_f32 and
-// dotted by v_dot2 (the G query heads share each loaded row); the rotated query
-// operands sit in LDS, and the rows of the next pass are loaded before the
-// current pass is computed. In the value phase D/4 lanes per row, a lane
-// holding elements [4s, 4s+4), 8 rows per pass. The kernel is held
+// rotation needs no lane exchange and the per-row reduction is 3 (d=128) DPP
+// steps; bf16 operands are rounded and packed by v_cvt_pk_bf16_f32 and dotted
+// by v_dot2 (the G query heads share each loaded row; their rotated operands
+// sit in LDS). Each chunk of candidates first gets a candidate -> row table in
+// LDS, read by the row loads, the selection and the value phase. Row loads are
+// double-buffered and never behind a branch, so the next pass's rows stay in
+// flight while the current one is computed. In the value phase D/4 lanes per
+// row, a lane holding elements [4s, 4s+4), 8 rows per pass. The kernel is held
 // to 128 VGPRs (4 waves per SIMD) for groups of up to 4 query heads.
 #include <math.h>
 
