@@ -255,3 +255,25 @@ def test_prefill_with_incremental_tree():
     pos = [0, 3, 4, 15, 16, 63, 64, 699, 700, 701, 2047, 2048, 2999] + list(range(1200, 1230))
     units = [(0, p, h) for p in pos for h in range(2)]
     _check_units(w, inp, (out, lse, sel, None), k, units, "prefill", q_start=0)
+
+
+def test_prefill_two_sequences_bf16_eight_head_groups():
+    """bf16 prefill of two sequences with 8 query heads per KV head, tree and queries in two
+    uneven calls: both sequences against the oracle at block edges and random positions."""
+    w = _w("pf_b2_g8", B=2, Hq=16, Hkv=2, d=128, dtype="bf16", L=3000, f=16, k=8, n_queries=3000, seed=33)
+    inp = gen_decode_inputs(w)
+    g = Gpu(w, inp, build=False)
+    from long_context_hierarchical_amd import recsa as R
+    k = [8] * 2
+    outs = []
+    for a, b in ((0, 1777), (1777, w.L)):
+        R.recsa_build_tree(g.shape, g.K, g.V, g.W, a, b, g.tree)
+        outs.append(g.prefill(k, a, b - a))
+    sel = np.concatenate([o[2] for o in outs], axis=1)
+    out = np.concatenate([o[0] for o in outs], axis=1)
+    lse = np.concatenate([o[1] for o in outs], axis=1)
+    rng = np.random.default_rng(3)
+    pos = sorted(set([0, 15, 16, 255, 256, 1776, 1777, 2047, 2048, 2999] + rng.integers(0, w.L, 12).tolist()))
+    units = [(b, p, h) for b in range(w.B) for p in pos for h in range(w.Hkv)]
+    _check_units(w, inp, (out, lse, sel, None), k, units, "prefill", q_start=0)
+
