@@ -153,18 +153,32 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(DenseArgs a) {
     for (int c = tid; c < KT * (D / 8); c += 256) {
       const int r = c / (D / 8), ch = c % (D / 8);
       const int64_t key = k0 + r;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (key < k_hi) {
+      uint4 kv = make_uint4(0, 0, 0, 0);
+      if (key < k_hi)
         kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Kr) + (bh * a.kr_rows + key) * D + ch * 8);
-        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.V) + (bh * a.v_rows + key) * D + ch * 8);
-      }
       *reinterpret_cast<uint4*>(&Ks[r * KPAD + ch * 8]) = kv;
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+    }
+    // V^T: a thread transposes a block of 4 keys x 4 dimensions in registers and writes 4
+    // dimension rows of 4 keys (8 bytes each); key quads vary fastest across lanes, so 16 lanes
+    // write 128 contiguous bytes of one row
+    for (int u = tid; u < (KT / 4) * (D / 4); u += 256) {
+      const int kq = u % (KT / 4), g = u / (KT / 4);
+      uint2 x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(ch * 8 + 2 * e) * VPAD + r] = static_cast<uint16_t>(w[e] & 0xFFFFu);
-        Vt[(ch * 8 + 2 * e + 1) * VPAD + r] = static_cast<uint16_t>(w[e] >> 16);
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t key = k0 + 4 * kq + jj;
+        x[jj] = make_uint2(0u, 0u);
+        if (key < k_hi)
+          x[jj] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.V) + (bh * a.v_rows + key) * D + 4 * g);
       }
+      uint16_t* vt = &Vt[(4 * g) * VPAD + 4 * kq];
+      *reinterpret_cast<uint2*>(vt) = make_uint2((x[0].x & 0xFFFFu) | (x[1].x << 16), (x[2].x & 0xFFFFu) | (x[3].x << 16));
+      *reinterpret_cast<uint2*>(vt + VPAD) =
+          make_uint2((x[0].x >> 16) | (x[1].x & 0xFFFF0000u), (x[2].x >> 16) | (x[3].x & 0xFFFF0000u));
+      *reinterpret_cast<uint2*>(vt + 2 * VPAD) =
+          make_uint2((x[0].y & 0xFFFFu) | (x[1].y << 16), (x[2].y & 0xFFFFu) | (x[3].y << 16));
+      *reinterpret_cast<uint2*>(vt + 3 * VPAD) =
+          make_uint2((x[0].y >> 16) | (x[1].y & 0xFFFF0000u), (x[2].y >> 16) | (x[3].y & 0xFFFF0000u));
     }
     __syncthreads();
 
