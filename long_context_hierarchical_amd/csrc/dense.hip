@@ -10,7 +10,8 @@
 //                (query, head) rows -- 16/G queries x the G heads of one KV head -- and the 4
 //                waves of a workgroup share every K/V tile staged in LDS. Scores are computed
 //                transposed, S^T = K Q~^T, so that each lane's probabilities are already in the
-//                operand layout of O^T += V^T P^T (V staged transposed in LDS); the online
+//                operand layout of O^T += V^T P^T; V is staged in LDS as stored (key-major) and
+//                the V^T operand is read with gfx950's transposing LDS load. The online
 //                softmax needs two lane exchanges per tile. Long key ranges are split across
 //                workgroups and merged afterwards. float32 storage: a plain VALU kernel.
 #include <math.h>
@@ -22,6 +23,16 @@ namespace recsa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+
+// ds_read_b64_tr_b16: within each 16-lane block, lane l receives element l % 4 of the 8-byte
+// chunks addressed by lanes l / 4, 4 + l / 4, 8 + l / 4, 12 + l / 4 of that block. When those
+// lanes point at 4 consecutive rows of a row-major bf16 tile (lane 4j + c at row j, columns
+// 4c .. 4c + 3), lane l gets column l of the 4 rows: the k-contiguous MFMA operand layout.
+__device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+}
 
 __device__ __forceinline__ void rope_cs(int64_t p, float w, float& c, float& s) {
   double sd, cd;
@@ -97,9 +108,11 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(DenseArgs a) {
   constexpr int DT = D / 16;           // 16-dim output tiles
   constexpr int HALF = D / 2;
   constexpr int KPAD = D + 8;          // K tile row stride (bf16)
-  constexpr int VPAD = KT + 8;         // V^T tile row stride (bf16)
+  // V tile row stride (bf16): D/2 + 8 dwords, an odd multiple of 8, so the 8 rows that 32
+  // lanes of a transposing read touch fall in distinct bank groups
+  constexpr int VPAD = D + 16;
   __shared__ __align__(16) uint16_t Ks[KT * KPAD];
-  __shared__ __align__(16) uint16_t Vt[D * VPAD];
+  __shared__ __align__(16) uint16_t Vs[KT * VPAD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -153,32 +166,13 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(DenseArgs a) {
     for (int c = tid; c < KT * (D / 8); c += 256) {
       const int r = c / (D / 8), ch = c % (D / 8);
       const int64_t key = k0 + r;
-      uint4 kv = make_uint4(0, 0, 0, 0);
-      if (key < k_hi)
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (key < k_hi) {
         kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Kr) + (bh * a.kr_rows + key) * D + ch * 8);
-      *reinterpret_cast<uint4*>(&Ks[r * KPAD + ch * 8]) = kv;
-    }
-    // V^T: a thread transposes a block of 4 keys x 4 dimensions in registers and writes 4
-    // dimension rows of 4 keys (8 bytes each); key quads vary fastest across lanes, so 16 lanes
-    // write 128 contiguous bytes of one row
-    for (int u = tid; u < (KT / 4) * (D / 4); u += 256) {
-      const int kq = u % (KT / 4), g = u / (KT / 4);
-      uint2 x[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int64_t key = k0 + 4 * kq + jj;
-        x[jj] = make_uint2(0u, 0u);
-        if (key < k_hi)
-          x[jj] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.V) + (bh * a.v_rows + key) * D + 4 * g);
+        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.V) + (bh * a.v_rows + key) * D + ch * 8);
       }
-      uint16_t* vt = &Vt[(4 * g) * VPAD + 4 * kq];
-      *reinterpret_cast<uint2*>(vt) = make_uint2((x[0].x & 0xFFFFu) | (x[1].x << 16), (x[2].x & 0xFFFFu) | (x[3].x << 16));
-      *reinterpret_cast<uint2*>(vt + VPAD) =
-          make_uint2((x[0].x >> 16) | (x[1].x & 0xFFFF0000u), (x[2].x >> 16) | (x[3].x & 0xFFFF0000u));
-      *reinterpret_cast<uint2*>(vt + 2 * VPAD) =
-          make_uint2((x[0].y & 0xFFFFu) | (x[1].y << 16), (x[2].y & 0xFFFFu) | (x[3].y << 16));
-      *reinterpret_cast<uint2*>(vt + 3 * VPAD) =
-          make_uint2((x[0].y >> 16) | (x[1].y & 0xFFFF0000u), (x[2].y >> 16) | (x[3].y & 0xFFFF0000u));
+      *reinterpret_cast<uint4*>(&Ks[r * KPAD + ch * 8]) = kv;
+      *reinterpret_cast<uint4*>(&Vs[r * VPAD + ch * 8]) = vv;
     }
     __syncthreads();
 
@@ -235,13 +229,15 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(DenseArgs a) {
         pb[i] = static_cast<__bf16>(sv[2 * kb][i]);
         pb[4 + i] = static_cast<__bf16>(sv[2 * kb + 1][i]);
       }
+      // this lane addresses key 32kb + 4*g4 + r16/4 (and 16 keys on), dims 16t + 4*(r16%4) + 0..3;
+      // it receives dim 16t + r16 of keys 32kb + 4*g4 + 0..3 and 32kb + 16 + 4*g4 + 0..3
+      const uint16_t* vr = &Vs[(32 * kb + 4 * g4 + (r16 >> 2)) * VPAD + 4 * (r16 & 3)];
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const uint16_t* vr = &Vt[(16 * t + r16) * VPAD + 32 * kb + 4 * g4];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-        const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, o[t], 0, 0, 0);
+        const i16x4_t lo = lds_read_tr16(vr + 16 * t);
+        const i16x4_t hi = lds_read_tr16(vr + 16 * VPAD + 16 * t);
+        const i16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, o[t], 0, 0, 0);
       }
     }
   }
