@@ -14,6 +14,7 @@ from .recsa import (  # noqa: F401
     decode,
     dense_unit,
     from_storage,
+    generate,
     inv_freq,
     level_counts,
     plan_counts,

@@ -413,3 +413,50 @@ def prefill(K, V, W, q, q_start: int, f: int, k_levels, dtype: str, theta: float
         out[(b, j, h)] = attend_unit(qg, Kf, Vf, tree, t + 1, f, k_levels, dtype, theta, scale,
                                      self_in=True)
     return out
+
+
+def generate(K, V, W, q_steps, k_steps, v_steps, n_start: int, f: int, k_levels, dtype: str,
+             theta: float = 1.0e6, scale=None):
+    """Autoregressive decoding over a growing cache.
+
+    [Abstract]: the tree is kept over the KV cache and attention costs
+    O(log L) per decoding step; [Core Idea]: nodes summarise complete spans of
+    the cache. Reading: each generated token first joins the cache, the nodes
+    its arrival completes are built (bottom level first, so a completed node
+    can complete its parent), and the token's query then attends over the
+    whole prefix, its own token included -- the causal semantics of prefill
+    for one position.
+
+    Step s handles position t = n_start + s: K[b, h, t] = k_steps[s, b, h] and
+    V likewise, the nodes complete at t + 1 but not at t are built, and
+    q_steps[s, b] (the G heads of each KV head) attends over tokens 0..t.
+
+    K, V: [B][Hkv][cap][d] storage form, holding at least the first n_start
+    tokens (not modified: each slice is copied); q_steps [S][B][Hq][d];
+    k_steps, v_steps [S][B][Hkv][d]; W [d][d] storage form.
+    Returns (results, slices): results[s][(b, h)] is the UnitResult of step s,
+    slices[(b, h)] = (K, V, tree) as float32 after the last step.
+    """
+    B, Hkv, cap, d = K.shape
+    S = q_steps.shape[0]
+    G = q_steps.shape[2] // Hkv
+    if n_start < 0 or n_start + S > cap:
+        raise ValueError("positions n_start .. n_start + S - 1 must lie inside the cache")
+    Wf = from_storage(W, dtype)
+    results = [dict() for _ in range(S)]
+    slices = {}
+    for b in range(B):
+        for h in range(Hkv):
+            Kf = from_storage(K[b, h], dtype).copy()
+            Vf = from_storage(V[b, h], dtype).copy()
+            tree = build_slice(Kf, Vf, Wf, f, dtype, n_new=n_start, cap=cap)
+            for s in range(S):
+                t = n_start + s
+                Kf[t] = from_storage(k_steps[s, b, h], dtype)
+                Vf[t] = from_storage(v_steps[s, b, h], dtype)
+                build_slice(Kf, Vf, Wf, f, dtype, n_new=t + 1, n_old=t, tree=tree, cap=cap)
+                qg = from_storage(q_steps[s, b, h * G:(h + 1) * G], dtype)
+                results[s][(b, h)] = attend_unit(qg, Kf, Vf, tree, t + 1, f, k_levels, dtype, theta, scale,
+                                                 self_in=True)
+            slices[(b, h)] = (Kf, Vf, tree)
+    return results, slices

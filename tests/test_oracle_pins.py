@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (INT32_MAX, attend_unit, bf16_round, build_slice, dense_unit, level_counts,
-                    plan_counts, rope_table, rotate)
+from oracle import (INT32_MAX, attend_unit, bf16_round, build_slice, dense_unit, from_storage, generate,
+                    level_counts, plan_counts, rope_table, rotate, to_storage)
 from brute64 import brute_unit, dense_textbook, rot as rot64
 from synthetic import bf16_bits, bf16_value
 
@@ -399,3 +399,88 @@ def test_pooler_follows_its_rounding_exactly(f, d, seed, dtype):
             for j in range(d):
                 acc = _rn32(Fraction(float(W[i, j])) * Fraction(float(m[j])) + Fraction(float(acc)))
             assert store(acc).view(np.uint32) == NK[n, i].view(np.uint32), (n, i)
+
+
+# ------------------------------------------------------------------ autoregressive decoding
+
+def _gen_case(seed, dtype="f32", pruned=True):
+    """Tiny generation run: S steps from n_start, long enough for a completion cascade through
+    three levels (t + 1 a multiple of f^3)."""
+    rng = np.random.default_rng(2000 + seed)
+    f = [2, 3, 4][seed % 3]
+    d, B, Hkv, G = 8, 1, 2, 2
+    n_start = int(rng.integers(0, 2 * f ** 2))
+    S = f ** 3 + 4
+    cap = n_start + S + int(rng.integers(0, 3))
+    std = 1.0 if dtype == "f32" else 0.5
+    K = _rand(rng, (B, Hkv, cap, d), std, dtype)
+    V = _rand(rng, (B, Hkv, cap, d), std, dtype)
+    q = _rand(rng, (S, B, Hkv * G, d), std, dtype)
+    kn = _rand(rng, (S, B, Hkv, d), std, dtype)
+    vn = _rand(rng, (S, B, Hkv, d), std, dtype)
+    W = (np.eye(d) + 0.3 / np.sqrt(d) * rng.standard_normal((d, d))).astype(np.float32)
+    if dtype == "bf16":
+        W = bf16_value(bf16_bits(W))
+    k = [int(rng.integers(1, f + 1)) for _ in range(6)] if pruned else [INT32_MAX] * 6
+    theta = [0.0, 50.0, 1.0e6][seed % 3]
+    return f, d, G, n_start, S, K, V, q, kn, vn, W, k, theta
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_generate_matches_float64_brute_force(seed):
+    """Every step of autoregressive decoding (f32) vs the independent float64 formulation over the
+    prefix 0..t with the query's own token included: selections level by level (unless a near tie),
+    outputs within 1e-6. A token written at the wrong row, a missed completion or a query that does
+    not see its own token changes the entries."""
+    f, d, G, n_start, S, K, V, q, kn, vn, W, k, theta = _gen_case(seed)
+    res, slices = generate(K, V, W, q, kn, vn, n_start, f, k, "f32", theta)
+    compared = 0
+    for s in range(S):
+        t = n_start + s
+        for (b, h), r in res[s].items():
+            Kf, Vf, _ = slices[(b, h)]
+            br = brute_unit(q[s, b, h * G:(h + 1) * G], Kf, Vf, W, t + 1, f, k, theta, self_in=True)
+            T = len(level_counts(t + 1, f))
+            if any(r.flags.get(lv) or br["gap"].get(lv, 1.0) < 1e-5 for lv in range(1, T + 1)):
+                continue
+            for lv in range(T, 0, -1):
+                assert r.sel[lv] == br["sel"][lv], f"step {s} level {lv}"
+            assert sorted(r.entries) == sorted(br["entries"])
+            assert any((lv, t // f ** lv) in r.entries for lv in range(T + 1))  # own token covered once
+            np.testing.assert_allclose(r.out, br["out"], rtol=0, atol=1e-6)
+            np.testing.assert_allclose(r.lse, br["lse"], rtol=0, atol=1e-6)
+            compared += 1
+    assert compared >= S  # most (step, head) units are compared, not skipped on near ties
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_generate_without_pruning_is_causal_dense(seed):
+    """Keeping everything at every level makes each step textbook RoPE attention of the token at t
+    over keys 0..t, the appended rows included."""
+    f, d, G, n_start, S, K, V, q, kn, vn, W, k, theta = _gen_case(seed, pruned=False)
+    res, slices = generate(K, V, W, q, kn, vn, n_start, f, k, "f32", theta)
+    for s in range(S):
+        t = n_start + s
+        for (b, h), r in res[s].items():
+            Kf, Vf, _ = slices[(b, h)]
+            np.testing.assert_array_equal(Kf[t], kn[s, b, h])
+            out, lse = dense_textbook(q[s, b, h * G:(h + 1) * G], Kf, Vf, t + 1, t, theta)
+            np.testing.assert_allclose(r.out, out, rtol=0, atol=1e-6)
+            np.testing.assert_allclose(r.lse, lse, rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_generate_tree_is_one_shot_tree(dtype):
+    """Nodes never change once complete, so the tree after S appended tokens is bitwise the tree
+    built in one pass over the final cache; the caller's arrays are left untouched."""
+    f, d, G, n_start, S, K, V, q, kn, vn, W, k, theta = _gen_case(4, dtype)
+    Ks, Vs = K.copy(), V.copy()
+    if dtype == "bf16":
+        K, V, q, kn, vn, W = (to_storage(x, "bf16") for x in (K, V, q, kn, vn, W))
+    _, slices = generate(K, V, W, q, kn, vn, n_start, f, k, dtype, theta)
+    for (b, h), (Kf, Vf, tree) in slices.items():
+        one = build_slice(Kf, Vf, from_storage(W, dtype), f, dtype, n_new=n_start + S, cap=Kf.shape[0])
+        for (k1, v1), (k2, v2) in zip(one, tree):
+            assert np.array_equal(k1.view(np.uint32), k2.view(np.uint32))
+            assert np.array_equal(v1.view(np.uint32), v2.view(np.uint32))
+    assert np.array_equal(from_storage(K, dtype), Ks) and np.array_equal(from_storage(V, dtype), Vs)
