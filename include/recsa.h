@@ -154,6 +154,31 @@ int32_t recsa_prefill(const recsa_shape_t* shape, const void* q, int64_t q_start
                       float* out, float* lse, int32_t* sel, int32_t sel_width,
                       void* workspace, int64_t ws_bytes, void* stream);
 
+/* One step of autoregressive decoding [Abstract: the tree kept over the KV cache, logarithmic
+ * cost per decoding step; Core Idea: nodes summarise complete spans of the cache]. Three parts,
+ * in order, on `stream`:
+ *   1. append: K[b][h][n_tokens] = k_new[b][h] and V[b][h][n_tokens] = v_new[b][h];
+ *   2. build: the nodes complete at n_tokens + 1 but not at n_tokens -- at most one per level,
+ *      bottom level first, each a parent of the one below -- with recsa_build_tree's arithmetic
+ *      (the tree must already hold every node complete at n_tokens);
+ *   3. attend: q, the new token's query at position n_tokens, over tokens 0..n_tokens with its
+ *      own token included: recsa_prefill with q_start = n_tokens and n_q = 1.
+ * Calling it for n_tokens = n, n + 1, ... gives, bit for bit, the caches, tree and outputs that
+ * writing the tokens, recsa_build_tree and recsa_prefill give for the same positions.
+ *   q [dev]: [B][H_q][d]; k_new, v_new [dev]: [B][H_kv][d] pre-RoPE, storage type, not inside K or V;
+ *   K, V [dev]: [B][H_kv][capacity][d], written at row n_tokens; W [dev]: [d][d] pooler;
+ *   tree [dev]: updated in place; out float32 [B][H_q][d]; lse float32 [B][H_q] (nullable);
+ *   sel [dev] (nullable): int32 [B][H_kv][n_levels][sel_width],
+ *   sel_width >= recsa_sel_width(n_tokens + 1, n_tokens + 1);
+ *   workspace: recsa_workspace_bytes(shape, n_tokens + 1, k, n_levels).
+ * Errors: as recsa_prefill; CAPACITY when n_tokens + 1 > capacity; INVALID_ARG when k_new or
+ * v_new overlaps a cache. Nothing is written when an error is returned. */
+int32_t recsa_decode_step(const recsa_shape_t* shape, const void* q, const void* k_new, const void* v_new,
+                          void* K, void* V, const void* W, void* tree, int64_t n_tokens,
+                          const int32_t* k_per_level, int32_t n_levels,
+                          float* out, float* lse, int32_t* sel, int32_t sel_width,
+                          void* workspace, int64_t ws_bytes, void* stream);
+
 /* Dense softmax attention with standard RoPE at the original positions -- the comparator the
  * method is timed against [Abstract]; also RecSA's limit when every level keeps everything.
  * mode: RECSA_DENSE_CAUSAL (bit 0) and/or RECSA_DENSE_KEYS_ROTATED (bit 1).

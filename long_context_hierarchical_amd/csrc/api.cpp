@@ -160,11 +160,21 @@ int32_t fill_table(const Info& I, int64_t P, void* ws, hipStream_t st) {
   return RECSA_OK;
 }
 
-int32_t run_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, const void* K, const void* V,
-                   const void* tree, int64_t n_fixed, int64_t q_start, bool prefill, const int32_t* k,
-                   int32_t n_levels, float* out, float* lse, int32_t* sel, int32_t sel_width, void* ws,
-                   int64_t ws_bytes, void* stream) {
+// A validated attention call: its kernel arguments, LDS bytes and RoPE table rows.
+struct AttendPlan {
   Info I;
+  recsa::AttnArgs a{};
+  size_t lds = 0;
+  int64_t P = 0;
+  bool empty = false;  // nothing to launch (no queries)
+};
+
+// Validates one decode / prefill call and fills its plan; launches nothing.
+int32_t prepare_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, const void* K, const void* V,
+                       const void* tree, int64_t n_fixed, int64_t q_start, bool prefill, const int32_t* k,
+                       int32_t n_levels, float* out, float* lse, int32_t* sel, int32_t sel_width, void* ws,
+                       int64_t ws_bytes, AttendPlan* pl) {
+  Info& I = pl->I;
   int32_t rc = check_shape(shape, &I);
   if (rc) return rc;
   if (n_q < 0) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 0");
@@ -177,7 +187,10 @@ int32_t run_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, const
                                  (long long)I.cap);
   rc = check_k(k, n_levels, levels_of(n_max, I.f));
   if (rc) return rc;
-  if (n_q == 0) return RECSA_OK;
+  if (n_q == 0) {
+    pl->empty = true;
+    return RECSA_OK;
+  }
   if (!q || !out || (n_max > 0 && (!K || !V)) || (levels_of(n_max, I.f) > 0 && !tree))
     return fail(RECSA_ERR_INVALID_ARG, "q, K, V, tree or out is NULL");
   if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(tree) || !aligned16(out) || !aligned16(ws))
@@ -202,11 +215,9 @@ int32_t run_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, const
   if (ws_bytes < need_ws) return fail(RECSA_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes, (long long)need_ws);
   if (need_ws > 0 && !ws) return fail(RECSA_ERR_INVALID_ARG, "workspace is NULL");
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = fill_table(I, bd.P, ws, st);
-  if (rc) return rc;
-
-  recsa::AttnArgs a{};
+  pl->lds = lds;
+  pl->P = bd.P;
+  recsa::AttnArgs& a = pl->a;
   a.q = q;
   a.K = K;
   a.V = V;
@@ -235,9 +246,28 @@ int32_t run_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, const
     a.tree.NV[lv] = static_cast<const char*>(tree) + level_offset_bytes(I, lv, 1);
     a.tree.rows[lv] = nodes_at(I.cap, I.f, lv);
   }
-  hipError_t e = recsa::launch_attend(a, static_cast<int>(I.d), I.bf16, static_cast<int>(I.G), lds, I.B, st);
+  return RECSA_OK;
+}
+
+int32_t launch_planned_attend(const AttendPlan& pl, hipStream_t st) {
+  hipError_t e = recsa::launch_attend(pl.a, static_cast<int>(pl.I.d), pl.I.bf16, static_cast<int>(pl.I.G), pl.lds,
+                                      pl.I.B, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return RECSA_OK;
+}
+
+int32_t run_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, const void* K, const void* V,
+                   const void* tree, int64_t n_fixed, int64_t q_start, bool prefill, const int32_t* k,
+                   int32_t n_levels, float* out, float* lse, int32_t* sel, int32_t sel_width, void* ws,
+                   int64_t ws_bytes, void* stream) {
+  AttendPlan pl;
+  int32_t rc = prepare_attend(shape, q, n_q, K, V, tree, n_fixed, q_start, prefill, k, n_levels, out, lse, sel,
+                              sel_width, ws, ws_bytes, &pl);
+  if (rc || pl.empty) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = fill_table(pl.I, pl.P, ws, st);
+  if (rc) return rc;
+  return launch_planned_attend(pl, st);
 }
 
 }  // namespace
@@ -356,6 +386,67 @@ int32_t recsa_prefill(const recsa_shape_t* shape, const void* q, int64_t q_start
                       int32_t* sel, int32_t sel_width, void* workspace, int64_t ws_bytes, void* stream) {
   return run_attend(shape, q, n_q, K, V, tree, 0, q_start, true, k, n_levels, out, lse, sel, sel_width, workspace,
                     ws_bytes, stream);
+}
+
+int32_t recsa_decode_step(const recsa_shape_t* shape, const void* q, const void* k_new, const void* v_new, void* K,
+                          void* V, const void* W, void* tree, int64_t n_tokens, const int32_t* k, int32_t n_levels,
+                          float* out, float* lse, int32_t* sel, int32_t sel_width, void* workspace, int64_t ws_bytes,
+                          void* stream) {
+  Info I;
+  int32_t rc = check_shape(shape, &I);
+  if (rc) return rc;
+  if (n_tokens < 0) return fail(RECSA_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (n_tokens + 1 > I.cap)
+    return fail(RECSA_ERR_CAPACITY, "the new token's row %lld is beyond the capacity %lld", (long long)n_tokens,
+                (long long)I.cap);
+  if (!k_new || !v_new || !K || !V || !W) return fail(RECSA_ERR_INVALID_ARG, "k_new, v_new, K, V or W is NULL");
+  if (levels_of(n_tokens + 1, I.f) > 0 && !tree) return fail(RECSA_ERR_INVALID_ARG, "tree is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(W))
+    return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  AttendPlan pl;
+  rc = prepare_attend(shape, q, 1, K, V, tree, 0, n_tokens, true, k, n_levels, out, lse, sel, sel_width, workspace,
+                      ws_bytes, &pl);
+  if (rc) return rc;
+  const char* kn = static_cast<const char*>(k_new);
+  const char* vn = static_cast<const char*>(v_new);
+  const int64_t row_bytes = I.B * I.Hkv * I.d * I.esz;
+  const int64_t cache_bytes = I.B * I.Hkv * I.cap * I.d * I.esz;
+  auto overlaps = [](const char* p, int64_t pn, const void* c, int64_t cn) {
+    const char* cc = static_cast<const char*>(c);
+    return p < cc + cn && cc < p + pn;
+  };
+  if (overlaps(kn, row_bytes, K, cache_bytes) || overlaps(kn, row_bytes, V, cache_bytes) ||
+      overlaps(vn, row_bytes, K, cache_bytes) || overlaps(vn, row_bytes, V, cache_bytes))
+    return fail(RECSA_ERR_INVALID_ARG, "k_new and v_new must not overlap the caches");
+
+  recsa::StepArgs sa{};
+  sa.k_new = k_new;
+  sa.v_new = v_new;
+  sa.K = K;
+  sa.V = V;
+  sa.cap = I.cap;
+  sa.n = n_tokens;
+  sa.W = W;
+  const int Tc = levels_of(I.cap, I.f);
+  for (int lv = 1; lv <= Tc && lv <= RECSA_MAX_LEVELS; ++lv) {
+    sa.NK[lv] = static_cast<char*>(tree) + level_offset_bytes(I, lv, 0);
+    sa.NV[lv] = static_cast<char*>(tree) + level_offset_bytes(I, lv, 1);
+    sa.rows[lv] = nodes_at(I.cap, I.f, lv);
+  }
+  sa.levels = std::min(Tc, RECSA_MAX_LEVELS);
+  sa.f = static_cast<int32_t>(I.f);
+  sa.BH = static_cast<int32_t>(I.B * I.Hkv);
+  sa.half = static_cast<int32_t>(I.d / 2);
+  if (I.theta != 0.0f) {
+    sa.tab = static_cast<float2*>(workspace);
+    sa.P = pl.P;
+    for (int i = 0; i < I.d / 2; ++i)
+      sa.iv.w[i] = static_cast<float>(std::pow(static_cast<double>(I.theta), -2.0 * i / static_cast<double>(I.d)));
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = recsa::launch_append_step(sa, static_cast<int>(I.d), I.bf16, st);
+  if (e != hipSuccess) return hip_fail(e, "append step launch");
+  return launch_planned_attend(pl, st);
 }
 
 struct DensePlan {

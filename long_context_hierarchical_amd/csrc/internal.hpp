@@ -40,6 +40,31 @@ struct InvFreq {
 // tab[p * (d/2) + i] = (cos(p * omega_i), sin(p * omega_i)), evaluated in float64, for p = 0..P.
 hipError_t launch_rope_table(float2* tab, int64_t P, int half, const InvFreq& iv, hipStream_t s);
 
+// ---------------------------------------------------------------- decoding step
+// Workgroups 0..BH-1 (one per sequence x KV head) write the new token at row n of K and V and
+// build the nodes its arrival completes, at most one per level, bottom level first. Workgroups
+// BH.. of the same grid fill the RoPE table rows 0..P when `tab` is set.
+struct StepArgs {
+  const void* k_new;    // [B*H_kv][d]
+  const void* v_new;
+  void* K;              // [B*H_kv][cap][d]
+  void* V;
+  int64_t cap;
+  int64_t n;            // row of the new token
+  const void* W;        // [d][d] pooler
+  void* NK[RECSA_MAX_LEVELS + 1];  // index = level (1-based); [B*H_kv][rows[l]][d]
+  void* NV[RECSA_MAX_LEVELS + 1];
+  int64_t rows[RECSA_MAX_LEVELS + 1];
+  int32_t levels;       // levels the tree buffer holds
+  int32_t f;
+  int32_t BH;
+  int32_t half;         // d / 2
+  float2* tab;          // RoPE table or null
+  int64_t P;
+  InvFreq iv;
+};
+hipError_t launch_append_step(const StepArgs& a, int d, bool bf16, hipStream_t s);
+
 // ---------------------------------------------------------------- descent + softmax
 struct TreeLevels {
   const void* NK[RECSA_MAX_LEVELS + 1];  // index = level (1-based); [B*H_kv][rows[l]][d]

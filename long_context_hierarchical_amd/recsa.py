@@ -21,6 +21,7 @@ INT32_MAX = 2 ** 31 - 1
 EXPORTS = (
     "recsa_abi_version", "recsa_last_error", "recsa_num_levels", "recsa_tree_bytes", "recsa_level_offset",
     "recsa_sel_width", "recsa_workspace_bytes", "recsa_build_tree", "recsa_decode", "recsa_prefill",
+    "recsa_decode_step",
     "recsa_dense_workspace_bytes", "recsa_dense_ref_attn", "recsa_rotate_keys",
 )
 RECSA_DENSE_CAUSAL, RECSA_DENSE_KEYS_ROTATED = 1, 2
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "recsa_build_tree": (I32, [SP, P, P, P, I64, I64, P, P]),
             "recsa_decode": (I32, [SP, P, I64, P, P, P, I64, K, I32, P, P, P, I32, P, I64, P]),
             "recsa_prefill": (I32, [SP, P, I64, I64, P, P, P, K, I32, P, P, P, I32, P, I64, P]),
+            "recsa_decode_step": (I32, [SP, P, P, P, P, P, P, P, I64, K, I32, P, P, P, I32, P, I64, P]),
             "recsa_dense_workspace_bytes": (I64, [SP, I64, I64, I32]),
             "recsa_dense_ref_attn": (I32, [SP, P, I64, I64, P, P, I64, I32, P, P, P, I64, P]),
             "recsa_rotate_keys": (I32, [SP, P, I64, P, P]),
@@ -177,6 +179,15 @@ def recsa_prefill(shape: Shape, q, q_start: int, K, V, tree, k_levels, out, lse=
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().recsa_prefill(ctypes.byref(shape.c()), _p(q), q_start, n_q, _p(K), _p(V), _p(tree), k, nl,
                                _p(out), _p(lse), _p(sel), sel_width, _p(workspace), ws_bytes, _stream(stream)))
+
+
+def recsa_decode_step(shape: Shape, q, k_new, v_new, K, V, W, tree, n_tokens: int, k_levels, out, lse=None,
+                      sel=None, sel_width: int = 0, workspace=None, stream=None):
+    k, nl = _k(k_levels)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().recsa_decode_step(ctypes.byref(shape.c()), _p(q), _p(k_new), _p(v_new), _p(K), _p(V), _p(W),
+                                   _p(tree), n_tokens, k, nl, _p(out), _p(lse), _p(sel), sel_width,
+                                   _p(workspace), ws_bytes, _stream(stream)))
 
 
 def recsa_dense_ref_attn(shape: Shape, q, q_start: int, K, V, n_tokens: int, mode: int, out, lse=None,

@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     gen_kv_slice,
     gen_queries,
     gen_decode_inputs,
+    gen_new_tokens,
     needle_plan,
     with_overrides,
 )

@@ -23,6 +23,8 @@ clustered keys, needle keys planted along a query direction):
     rho = std * sqrt(d) (the background key norm) and u the unit direction of
     one target query head of that KV group.
   * pooler: W = I + (w_gain / sqrt(d)) * N(0, 1), rounded to the storage type.
+  * generated tokens (decoding past the end of a workload's cache): new keys
+    and values ~ N(0, std^2) per element, drawn per (sequence, KV head).
 """
 from __future__ import annotations
 
@@ -31,7 +33,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-_TAG_W, _TAG_K, _TAG_V, _TAG_Q, _TAG_CENTRE, _TAG_RUN, _TAG_QNOISE, _TAG_QCENTRE = range(1, 9)
+_TAG_W, _TAG_K, _TAG_V, _TAG_Q, _TAG_CENTRE, _TAG_RUN, _TAG_QNOISE, _TAG_QCENTRE, _TAG_NEWK, _TAG_NEWV = range(1, 11)
 
 
 @dataclass(frozen=True)
@@ -208,3 +210,15 @@ def gen_decode_inputs(w: Workload, n_q: int | None = None, heads=None, seqs=None
         for h in range(w.Hkv) if heads is None else heads:
             K[b, h], V[b, h] = gen_kv_slice(w, b, h, q[b])
     return {"K": K, "V": V, "q": q, "W": gen_W(w)}
+
+
+def gen_new_tokens(w: Workload, n_new: int):
+    """Keys and values of n_new tokens generated after the workload's L cached ones:
+    (k_new, v_new), each [n_new][B][Hkv][d] storage form, i.i.d. N(0, std^2)."""
+    k = np.empty((n_new, w.B, w.Hkv, w.d), dtype=np.float32)
+    v = np.empty_like(k)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            k[:, b, h] = _rng(w, _TAG_NEWK, b, h).standard_normal((n_new, w.d), dtype=np.float32) * np.float32(w.std)
+            v[:, b, h] = _rng(w, _TAG_NEWV, b, h).standard_normal((n_new, w.d), dtype=np.float32) * np.float32(w.std)
+    return _store(k, w.dtype), _store(v, w.dtype)

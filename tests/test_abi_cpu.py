@@ -72,9 +72,9 @@ def test_workspace_holds_the_rope_table():
     assert R.recsa_workspace_bytes(_shape(rope_theta=0.0), 131072, k) == 0
 
 
-def _status(fn, *args):
+def _status(fn, *args, **kw):
     with pytest.raises(R.RecsaError) as e:
-        fn(*args)
+        fn(*args, **kw)
     return e.value.code
 
 
@@ -124,3 +124,15 @@ def test_error_paths_return_status_before_launch():
     assert _status(R.recsa_decode, _shape(capacity=1 << 20), q, t, t, t, 1 << 20, [1 << 30] * 5, t, None, None, 0,
                    t, ns) == -3                                                          # lists beyond LDS
     assert "capacity" in R.lib().recsa_last_error().decode() or R.lib().recsa_last_error()
+    # one decoding step: the new row must fit, its inputs must lie outside the caches, the
+    # pooler is needed, and the attention checks apply -- all before anything is written
+    kn = _FakeTensor(0x10000000)
+    q1 = _FakeTensor(shape=(2, 32, 128))
+    step = R.recsa_decode_step
+    assert _status(step, sh, q1, kn, kn, t, t, t, t, 4096, k, t, workspace=t, stream=ns) == -2
+    assert _status(step, sh, q1, t, kn, t, t, t, t, 100, k, t, workspace=t, stream=ns) == -1
+    assert "overlap" in R.lib().recsa_last_error().decode()
+    assert _status(step, sh, q1, kn, kn, t, t, None, t, 100, k, t, workspace=t, stream=ns) == -1
+    assert _status(step, sh, q1, kn, kn, t, t, t, t, 4095, [8, 8], t, workspace=t, stream=ns) == -1
+    assert _status(step, sh, q1, kn, kn, t, t, t, t, 100, k, t, None, None, 0, small_ws, stream=ns) == -5
+    assert _status(step, sh, q1, kn, kn, t, t, t, t, 100, k, t, None, t, 0, t, stream=ns) == -1  # sel_width

@@ -8,7 +8,7 @@ import torch
 import oracle
 from gpu_util import TOL, Gpu, compare_unit, storage_bits
 from long_context_hierarchical_amd import recsa as R
-from synthetic import WORKLOADS, gen_kv_slice, gen_queries, gen_W
+from synthetic import WORKLOADS, gen_kv_slice, gen_new_tokens, gen_queries, gen_W
 
 pytestmark = pytest.mark.gpu
 
@@ -17,20 +17,21 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _upload_workload(w, n_q):
-    """K, V, q for the whole workload straight to the device, slice by slice; host keeps q only."""
+def _upload_workload(w, n_q, extra_rows=0):
+    """K, V, q for the whole workload straight to the device, slice by slice; host keeps q only.
+    `extra_rows` cache rows after the L tokens are left as NaN (for tokens generated later)."""
     dev = "cuda:0"
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    K = torch.empty(w.B, w.Hkv, w.L, w.d, dtype=td, device=dev)
-    V = torch.empty_like(K)
+    K = torch.full((w.B, w.Hkv, w.L + extra_rows, w.d), float("nan"), dtype=td, device=dev)
+    V = torch.full_like(K, float("nan"))
     qs = []
     for b in range(w.B):
         qb = gen_queries(w, b, n_q)
         qs.append(qb)
         for h in range(w.Hkv):
             Kb, Vb = gen_kv_slice(w, b, h, qb)
-            K[b, h] = torch.from_numpy(Kb).view(td).to(dev)
-            V[b, h] = torch.from_numpy(Vb).view(td).to(dev)
+            K[b, h, :w.L] = torch.from_numpy(Kb).view(td).to(dev)
+            V[b, h, :w.L] = torch.from_numpy(Vb).view(td).to(dev)
             _say(f"  {w.name}: slice ({b}, {h}) uploaded")
     q = np.stack(qs)
     qd = torch.from_numpy(q).view(td).to(dev)
@@ -128,3 +129,61 @@ def test_full_size_chunked_prefill_64k():
         stats[st] += 1
     _say(f"full prefill c3: {stats}")
     assert stats["match"] >= len(units) - 1
+
+
+def test_full_size_generation_2m():
+    """Autoregressive decoding at the 2M-token, fanout-32 shape, in the launch configuration the
+    benchmark times (one recsa_decode_step per token for every KV head): 8 steps from position
+    L - 4, across the four-level completion at t + 1 = 2^21. The first 4 steps re-append the
+    cache's own last tokens, the rest append generated ones; the oracle generates sampled
+    (sequence, KV head) slices step by step, and their caches and trees must match bit for bit."""
+    w = WORKLOADS["c4"]
+    S, n_start, G = 8, w.L - 4, w.G
+    _say("full generation c4: generating")
+    K, V, qd, Wd, q, W = _upload_workload(w, S, extra_rows=4)
+    dev = "cuda:0"
+    td = K.dtype
+    kx, vx = gen_new_tokens(w, S - 4)                                   # [4][B][Hkv][d]
+    kn = torch.cat([K[:, :, n_start:w.L].permute(2, 0, 1, 3), torch.from_numpy(kx).view(td).to(dev)]).contiguous()
+    vn = torch.cat([V[:, :, n_start:w.L].permute(2, 0, 1, 3), torch.from_numpy(vx).view(td).to(dev)]).contiguous()
+    qs = qd.transpose(0, 1).contiguous()                                # [S][B][Hq][d]
+    sh = R.Shape(w.B, w.Hkv, w.Hq, w.d, w.f, w.dtype, w.L + 4, 0.0, w.theta)
+    tree = torch.zeros(R.recsa_tree_bytes(sh), dtype=torch.uint8, device=dev)
+    R.recsa_build_tree(sh, K, V, Wd, 0, n_start, tree)
+    T = R.recsa_num_levels(w.L + 4, w.f)
+    k = [w.k] * T
+    width = R.recsa_sel_width(sh, n_start + 1, w.L + 4, k)
+    ws = torch.zeros(R.recsa_workspace_bytes(sh, w.L + 4, k), dtype=torch.uint8, device=dev)
+    out = torch.empty(S, w.B, w.Hq, w.d, dtype=torch.float32, device=dev)
+    lse = torch.empty(S, w.B, w.Hq, dtype=torch.float32, device=dev)
+    sel = torch.empty(S, w.B, w.Hkv, T, width, dtype=torch.int32, device=dev)
+    for s in range(S):
+        R.recsa_decode_step(sh, qs[s], kn[s], vn[s], K, V, Wd, tree, n_start + s, k, out[s], lse[s], sel[s], width, ws)
+    torch.cuda.synchronize()
+    _say("full generation c4: gpu done")
+    out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
+    stats = {"match": 0, "excused": 0}
+    for h in (0, 5):
+        Kb, Vb = gen_kv_slice(w, 0, h, q[0])
+        ks = np.concatenate([Kb[n_start:], kx[:, 0, h]])                # [S][d]
+        vs = np.concatenate([Vb[n_start:], vx[:, 0, h]])
+        Kc = np.concatenate([Kb, kx[:, 0, h]])[None, None]               # [1][1][L + 4][d]
+        Vc = np.concatenate([Vb, vx[:, 0, h]])[None, None]
+        qh = q[0, :S, h * G:(h + 1) * G][:, None]                        # [S][1][G][d]
+        res, slices = oracle.generate(Kc, Vc, W, qh, ks[:, None, None], vs[:, None, None], n_start, w.f, k, w.dtype,
+                                      w.theta)
+        for s in range(S):
+            st = compare_unit(res[s][(0, 0)], sel[s, 0, h], out[s, 0, h * G:(h + 1) * G], lse[s, 0, h * G:(h + 1) * G],
+                              TOL[w.dtype], where=f"c4 generation step {s} head {h}")
+            stats[st] += 1
+        Kf, Vf, tr = slices[(0, 0)]
+        for got, ref in ((storage_bits(K[0, h]), Kf), (storage_bits(V[0, h]), Vf)):
+            assert np.array_equal(got, oracle.to_storage(ref, w.dtype).view(got.dtype)), h
+        for lv in range(1, T + 1):
+            NK, NV = R.tree_level_views(sh, tree, lv)
+            for arr, ref in ((NK, tr[lv - 1][0]), (NV, tr[lv - 1][1])):
+                got = storage_bits(arr[0, h])
+                assert np.array_equal(got, oracle.to_storage(ref, w.dtype).view(got.dtype)), (h, lv)
+        _say(f"full generation c4: head {h} checked")
+    _say(f"full generation c4: {stats}")
+    assert stats["match"] >= 2 * S - 1
