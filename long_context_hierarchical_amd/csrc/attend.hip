@@ -294,9 +294,14 @@ struct RawV {
 // the waves share the score passes, wave 0 alone selects and computes the softmax weights,
 // and each wave owns D / NW of the value dimensions with the same row-group accumulation
 // chains as one wave, so every output element is accumulated in exactly the same order and
-// the results are bitwise those of NW = 1.
+// the results are bitwise those of NW = 1. When the launcher grants the LDS (pv_stage), the
+// value rows of a softmax chunk are staged through LDS by all threads with 16-byte loads
+// (the first round is in flight during wave 0's weight pass, each next one during the
+// current round's accumulation), and a lane reads its chain's rows 8 at a time without a
+// branch (a kept row has weight 0, and adding 0 * v leaves the sum unchanged). Occupancy
+// does not matter with so few units, so these kernels may take up to 256 registers.
 template <int D, bool BF16, int G, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2))) void attend_kernel(AttnArgs args) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1 && G <= 4 ? 4 : 2))) void attend_kernel(AttnArgs args) {
   // read the arguments in place: the per-level tables are indexed by a run-time level, and a
   // by-value copy of the struct would be placed in scratch memory
   (void)args;
@@ -309,6 +314,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
   constexpr int SPP = kWave / SL;      // rows per pass, score phase
   constexpr int HALF = D / 2;
   constexpr int PV_UNROLL = NW == 1 ? 4 : 8;
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int SCPR = D * ESZ / 16;   // 16-byte pieces per row, staged value rows
+  constexpr int SR = NW * kWave * 4 / SCPR;   // rows per staging round
+  static_assert(NW == 1 || SR % (8 * (kWave / (D / VE))) == 0, "a staging round holds whole 8-row residue steps");
   static_assert(VE % NW == 0, "waves split the value elements of a lane");
 
   extern __shared__ __align__(16) unsigned char lds[];
@@ -326,6 +335,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
   int32_t* selB = reinterpret_cast<int32_t*>(lds + L.selB);
   int64_t* nls = reinterpret_cast<int64_t*>(lds + L.nls);
   float* bc = reinterpret_cast<float*>(lds + L.bc);   // wave 0 -> all: alpha[G], l[G]
+  uint4* vst = reinterpret_cast<uint4*>(lds + L.total);   // staged value rows (several waves)
+  const bool staged = NW > 1 && a.pv_stage != 0;
 
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   const int tid = threadIdx.x;
@@ -612,6 +623,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
   const int dim0 = wid * (D / NW) + sub * VEW;
   auto softmax_pv = [&](const void* vsrc, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn,
                         bool use_flags) {
+    // several waves: value rows staged through LDS, 4 16-byte pieces per thread and round
+    uint4 st0, st1, st2, st3;
+    auto piece = [&](int32_t s0, int i) -> uint4 {
+      const int idx = tid + i * NT;
+      const int32_t r = s0 + idx / SCPR;
+      const int64_t row = rowbase + cid[r < cn ? r : cn - 1];
+      return *reinterpret_cast<const uint4*>(static_cast<const char*>(vsrc) + row * (D * ESZ) + (idx % SCPR) * 16);
+    };
+    auto stage_issue = [&](int32_t s0) {
+      st0 = piece(s0, 0);
+      st1 = piece(s0, 1);
+      st2 = piece(s0, 2);
+      st3 = piece(s0, 3);
+    };
+    if constexpr (NW > 1) {
+      if (staged) stage_issue(0);   // in flight during wave 0's weight pass
+    }
     if (wid == 0) {
       float mnew[G];
 #pragma unroll
@@ -661,6 +689,51 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(G <= 4 
 #pragma unroll
           for (int e = 0; e < VEW; ++e) acc[hh][e] *= alpha;
         }
+      }
+      if (staged) {
+        // rounds of SR rows through LDS; the next round's loads are in flight while this
+        // round is accumulated. Each lane keeps its chain: rows of its residue rg mod RPP in
+        // ascending order, element dim0 + e, as with one wave.
+        for (int32_t s0 = 0; s0 < cn; s0 += SR) {
+          vst[tid] = st0;
+          vst[tid + NT] = st1;
+          vst[tid + 2 * NT] = st2;
+          vst[tid + 3 * NT] = st3;
+          if (s0 + SR < cn) stage_issue(s0 + SR);
+          bsync();
+          const int32_t sn = cn - s0 < SR ? cn - s0 : SR;
+          // 8 rows of the residue per step, their LDS reads issued together and no branch: a
+          // kept row has weight 0 and a row past the end (a finite staged copy) gets weight 0,
+          // and fmaf(0, v, acc) leaves acc unchanged, exactly as skipping the row does
+          for (int32_t rb = 0; rb < sn; rb += 8 * RPP) {
+            float v[8][VEW], pz[8][G];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int32_t rr = rb + u * RPP + rg;
+              const bool ok = rr < sn;
+              if constexpr (BF16) {
+                const uint16_t* vp = reinterpret_cast<const uint16_t*>(vst) + rr * D + dim0;
+#pragma unroll
+                for (int e = 0; e < VEW; ++e) v[u][e] = __uint_as_float(static_cast<uint32_t>(vp[e]) << 16);
+              } else {
+                const float* vp = reinterpret_cast<const float*>(vst) + rr * D + dim0;
+#pragma unroll
+                for (int e = 0; e < VEW; ++e) v[u][e] = vp[e];
+              }
+              const int32_t r = s0 + (ok ? rr : 0);
+#pragma unroll
+              for (int hh = 0; hh < G; ++hh) pz[u][hh] = ok ? zs[hh * zcap + r] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+              for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+                for (int e = 0; e < VEW; ++e) acc[hh][e] = fmaf(pz[u][hh], v[u][e], acc[hh][e]);
+          }
+          bsync();
+        }
+        return;
       }
     }
     // value rows: two buffers alternate, the next iteration's rows are requested before this
@@ -790,7 +863,15 @@ template <int D, bool BF16, int G>
 static hipError_t launch_attend_t(const AttnArgs& a, size_t lds, int64_t B, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.n_q * a.Hkv), static_cast<unsigned>(B));
   if (a.n_q * a.Hkv * B < kMultiWaveUnits) {
-    hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds, s, a);
+    // value rows staged through LDS when it has room (4 waves x 64 lanes x 4 x 16 bytes)
+    constexpr size_t kStage = 4 * kWave * 4 * 16;
+    if (lds + kStage <= 65536) {
+      AttnArgs b = a;
+      b.pv_stage = 1;
+      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + kStage, s, b);
+    } else {
+      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds, s, a);
+    }
   } else {
     hipLaunchKernelGGL((attend_kernel<D, BF16, G, 1>), grid, dim3(kWave), lds, s, a);
   }

@@ -95,6 +95,7 @@ struct AttnArgs {
   int32_t use_rope;
   int32_t smax;         // capacity of a kept-node list
   int32_t zcap;         // capacity of a scored candidate list (selecting levels and token-level chunks)
+  int32_t pv_stage;     // set by the launcher: several waves per unit stage value rows through LDS
   LevelK k;
   TreeLevels tree;
 };
