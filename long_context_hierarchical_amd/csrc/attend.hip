@@ -127,7 +127,7 @@ __host__ __device__ inline Lds lds_layout(int d, int G, int smax, int zcap) {
   uint32_t o = 0;
   L.q = o;     o = align16(o + 4u * G * d);         // raw query heads of the KV group
   L.qr = o;    o = align16(o + 4u * G * d);         // rotated query operands of the current level
-  L.zs = o;    o = align16(o + 4u * G * zcap);      // logits, then softmax weights, [G][zcap]
+  L.zs = o;    o = align16(o + 4u * G * zcap);      // logits, then softmax weights, [zcap][G]
   L.sc = o;    o = align16(o + 4u * zcap);          // group scores
   L.cid = o;   o = align16(o + 4u * zcap);          // node (or token) id of each scored candidate
   L.flags = o; o = align16(o + zcap);               // kept flags
@@ -336,7 +336,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
   int64_t* nls = reinterpret_cast<int64_t*>(lds + L.nls);
   float* bc = reinterpret_cast<float*>(lds + L.bc);   // wave 0 -> all: alpha[G], l[G]
   uint4* vst = reinterpret_cast<uint4*>(lds + L.total);   // staged value rows (several waves)
-  const bool staged = NW > 1 && a.pv_stage != 0;
+  const bool staged = NW > 1 && a.pv_stage == 1;          // rounds of SR rows
+  const bool prefetched = NW > 1 && a.pv_stage == 2;      // a chunk's rows, loaded while it is scored
+  // the G logits (then weights) of candidate r: one vector LDS access
+  auto zrow_load = [&](int32_t r, float (&z)[G]) {
+    if constexpr (G % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < G / 4; ++i) {
+        const float4 t = reinterpret_cast<const float4*>(zs + r * G)[i];
+        z[4 * i] = t.x; z[4 * i + 1] = t.y; z[4 * i + 2] = t.z; z[4 * i + 3] = t.w;
+      }
+    } else if constexpr (G == 2) {
+      const float2 t = reinterpret_cast<const float2*>(zs + r * G)[0];
+      z[0] = t.x; z[1] = t.y;
+    } else {
+      z[0] = zs[r];
+    }
+  };
+  auto zrow_store = [&](int32_t r, const float (&z)[G]) {
+    if constexpr (G % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < G / 4; ++i)
+        reinterpret_cast<float4*>(zs + r * G)[i] = make_float4(z[4 * i], z[4 * i + 1], z[4 * i + 2], z[4 * i + 3]);
+    } else if constexpr (G == 2) {
+      reinterpret_cast<float2*>(zs + r * G)[0] = make_float2(z[0], z[1]);
+    } else {
+      zs[r] = z[0];
+    }
+  };
 
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
   const int tid = threadIdx.x;
@@ -448,31 +475,59 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     bsync();
   };
 
-  // logits of candidates [c0, c0 + cn) (index = RoPE position) -> zs[hh * zcap + r], sc[r].
+  // several waves, prefetch mode: the value rows of candidates [0, cn) -- rounded up to whole
+  // 8-row residue steps with copies of the last row -- go straight from memory to LDS
+  // (row-major, D * ESZ bytes a row) while the chunk is scored and selected
+  auto prefetch_values = [&](const void* vsrc, int64_t rowbase, int32_t cn) {
+    const int32_t pieces = ((cn + 8 * RPP - 1) / (8 * RPP)) * (8 * RPP) * SCPR;
+    for (int32_t jw = wid; jw * kWave < pieces; jw += NW) {
+      const int32_t idx = jw * kWave + lane;
+      const int32_t r = idx / SCPR;
+      const int64_t row = rowbase + cid[r < cn ? r : cn - 1];
+      const char* g = static_cast<const char*>(vsrc) + row * (D * ESZ) + (idx % SCPR) * 16;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
+                                       (__attribute__((address_space(3))) void*)(vst + jw * kWave), 16, 0, 0);
+    }
+  };
+  // logits of candidates [c0, c0 + cn) (index = RoPE position) -> zs[r * G + hh], sc[r].
   // Two row buffers alternate: the rows of the next pass are requested after this pass's
   // RoPE-table entries, so waiting for the table does not wait for them. The loop body has
   // no branch around a load (the rotation is chosen outside the loop; a pass past the end
   // and lanes past the last candidate load the last candidate's row and write nothing), so
   // the loads' completion is tracked exactly.
-  auto score_rows_t = [&](const void* src, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn, int64_t qpos,
-                          auto rope) {
+  auto score_rows_t = [&](const void* src, const void* vsrc, int64_t rowbase, const CandMap& cm, int32_t c0,
+                          int32_t cn, int64_t qpos, auto rope) {
     constexpr bool ROPE = decltype(rope)::value;
-    auto fetch = [&](int32_t r0, Raw8<BF16>& lo, Raw8<BF16>& hi) {
+    // several waves (latency-bound): a pass's RoPE-table entries are fetched with its rows,
+    // one pass ahead; one wave fetches them at the start of the pass (fewer registers)
+    constexpr bool PT = ROPE && NW > 1;
+    float4 ta[PT ? 4 : 1], tb[PT ? 4 : 1];
+    auto fetch = [&](int32_t r0, Raw8<BF16>& lo, Raw8<BF16>& hi, float4 (&tn)[PT ? 4 : 1]) {
       const int32_t r = r0 + srg < cn ? r0 + srg : cn - 1;
       const int64_t off = (rowbase + cid[r]) * D + 8 * ssub;
       lo = raw8_load<BF16>(src, off);
       hi = raw8_load<BF16>(src, off + HALF);
+      if constexpr (PT) {
+        const float4* t = reinterpret_cast<const float4*>(a.tab + static_cast<int64_t>(c0 + r) * HALF + 8 * ssub);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tn[u] = t[u];
+      }
     };
-    auto pass = [&](int32_t r0, const Raw8<BF16>& clo, const Raw8<BF16>& chi, Raw8<BF16>& nlo, Raw8<BF16>& nhi) {
+    auto pass = [&](int32_t r0, const Raw8<BF16>& clo, const Raw8<BF16>& chi, const float4 (&tc)[PT ? 4 : 1],
+                    Raw8<BF16>& nlo, Raw8<BF16>& nhi, float4 (&tn)[PT ? 4 : 1]) {
       const int32_t r = r0 + srg;
       const bool valid = r < cn;
       float4 tv[4];
-      if constexpr (ROPE) {
+      if constexpr (ROPE && !PT) {
         const float4* t = reinterpret_cast<const float4*>(a.tab + static_cast<int64_t>(c0 + (valid ? r : 0)) * HALF + 8 * ssub);
 #pragma unroll
         for (int u = 0; u < 4; ++u) tv[u] = t[u];
       }
-      fetch(r0 + NW * SPP, nlo, nhi);
+      fetch(r0 + NW * SPP, nlo, nhi, tn);
+      if constexpr (PT) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tv[u] = tc[u];
+      }
       float klo[8], khi[8];
       raw8_cvt<BF16>(clo, klo);
       raw8_cvt<BF16>(chi, khi);
@@ -528,34 +583,36 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) part[hh] = lane_group_sum<SL>(part[hh]);
       if (valid && ssub == 0) {
-        float S = 0.0f;
+        float S = 0.0f, z[G];
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          const float z = part[hh] * a.scale;
-          zs[hh * zcap + r] = z;
-          S = S + z;
+          z[hh] = part[hh] * a.scale;
+          S = S + z[hh];
         }
+        zrow_store(r, z);
         sc[r] = S;
       }
     };
     // the chunk's candidate -> row map, read by the row loads, the selection and the values
     for (int32_t r = tid; r < cn; r += NT) cid[r] = cm(c0 + r);
     bsync();
+    if (prefetched) prefetch_values(vsrc, rowbase, cn);
     Raw8<BF16> alo, ahi, blo, bhi;
     int32_t r0 = wid * SPP;
-    fetch(r0, alo, ahi);
+    fetch(r0, alo, ahi, ta);
     if (qpos >= 0) rotate_query(qpos);   // its table reads overlap the first rows' loads
     for (; r0 < cn; r0 += 2 * NW * SPP) {
-      pass(r0, alo, ahi, blo, bhi);
+      pass(r0, alo, ahi, ta, blo, bhi, tb);
       if (r0 + NW * SPP >= cn) break;
-      pass(r0 + NW * SPP, blo, bhi, alo, ahi);
+      pass(r0 + NW * SPP, blo, bhi, tb, alo, ahi, ta);
     }
     bsync();
   };
   // qpos >= 0: rotate the query heads at qpos first (a level's first chunk)
-  auto score_rows = [&](const void* src, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn, int64_t qpos) {
-    if (a.use_rope) score_rows_t(src, rowbase, cm, c0, cn, qpos, std::true_type{});
-    else score_rows_t(src, rowbase, cm, c0, cn, qpos, std::false_type{});
+  auto score_rows = [&](const void* src, const void* vsrc, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn,
+                        int64_t qpos) {
+    if (a.use_rope) score_rows_t(src, vsrc, rowbase, cm, c0, cn, qpos, std::true_type{});
+    else score_rows_t(src, vsrc, rowbase, cm, c0, cn, qpos, std::false_type{});
   };
   // Keeps the s largest (S, -r) keys among r < C: flags[r] = 1 and sel_out[0..s) = their
   // node ids in candidate order. A threshold is found by bisection on the scores'
@@ -639,6 +696,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     };
     if constexpr (NW > 1) {
       if (staged) stage_issue(0);   // in flight during wave 0's weight pass
+      // this wave's prefetched rows have landed in LDS before the barrier below
+      if (prefetched) __builtin_amdgcn_s_waitcnt(0);
     }
     if (wid == 0) {
       float mnew[G];
@@ -646,8 +705,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
       for (int hh = 0; hh < G; ++hh) mnew[hh] = -INFINITY;
       for (int32_t r = lane; r < cn; r += kWave) {
         if (use_flags && flags[r]) continue;
+        float z[G];
+        zrow_load(r, z);
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(mnew[hh], zs[hh * zcap + r]);
+        for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(mnew[hh], z[hh]);
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) mnew[hh] = fmaxf(m_run[hh], wave_max_dpp(mnew[hh]));
@@ -656,12 +717,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
       for (int hh = 0; hh < G; ++hh) ls[hh] = 0.0f;
       for (int32_t r = lane; r < cn; r += kWave) {
         const bool skip = use_flags && flags[r];
+        float z[G];
+        zrow_load(r, z);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          const float p = skip ? 0.0f : expf(zs[hh * zcap + r] - mnew[hh]);
-          zs[hh * zcap + r] = p;
+          const float p = skip ? 0.0f : expf(z[hh] - mnew[hh]);
+          z[hh] = p;
           ls[hh] += p;
         }
+        zrow_store(r, z);
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
@@ -690,6 +754,43 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
           for (int e = 0; e < VEW; ++e) acc[hh][e] *= alpha;
         }
       }
+      // 8 rows of the residue per step from LDS rows [0, sn) of vst (rows up to the next
+      // multiple of 8 * RPP hold finite copies), their reads issued together and no branch: a
+      // kept row has weight 0 and a row past the end gets weight 0, and fmaf(0, v, acc)
+      // leaves acc unchanged, exactly as skipping the row does
+      auto chains = [&](int32_t s0, int32_t sn) {
+        for (int32_t rb = 0; rb < sn; rb += 8 * RPP) {
+          float v[8][VEW], pz[8][G];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int32_t rr = rb + u * RPP + rg;
+            const bool ok = rr < sn;
+            if constexpr (BF16) {
+              const uint16_t* vp = reinterpret_cast<const uint16_t*>(vst) + rr * D + dim0;
+#pragma unroll
+              for (int e = 0; e < VEW; ++e) v[u][e] = __uint_as_float(static_cast<uint32_t>(vp[e]) << 16);
+            } else {
+              const float* vp = reinterpret_cast<const float*>(vst) + rr * D + dim0;
+#pragma unroll
+              for (int e = 0; e < VEW; ++e) v[u][e] = vp[e];
+            }
+            zrow_load(s0 + (ok ? rr : 0), pz[u]);
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) pz[u][hh] = ok ? pz[u][hh] : 0.0f;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+              for (int e = 0; e < VEW; ++e) acc[hh][e] = fmaf(pz[u][hh], v[u][e], acc[hh][e]);
+        }
+      };
+      if (prefetched) {
+        chains(0, cn);
+        bsync();
+        return;
+      }
       if (staged) {
         // rounds of SR rows through LDS; the next round's loads are in flight while this
         // round is accumulated. Each lane keeps its chain: rows of its residue rg mod RPP in
@@ -701,36 +802,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
           vst[tid + 3 * NT] = st3;
           if (s0 + SR < cn) stage_issue(s0 + SR);
           bsync();
-          const int32_t sn = cn - s0 < SR ? cn - s0 : SR;
-          // 8 rows of the residue per step, their LDS reads issued together and no branch: a
-          // kept row has weight 0 and a row past the end (a finite staged copy) gets weight 0,
-          // and fmaf(0, v, acc) leaves acc unchanged, exactly as skipping the row does
-          for (int32_t rb = 0; rb < sn; rb += 8 * RPP) {
-            float v[8][VEW], pz[8][G];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int32_t rr = rb + u * RPP + rg;
-              const bool ok = rr < sn;
-              if constexpr (BF16) {
-                const uint16_t* vp = reinterpret_cast<const uint16_t*>(vst) + rr * D + dim0;
-#pragma unroll
-                for (int e = 0; e < VEW; ++e) v[u][e] = __uint_as_float(static_cast<uint32_t>(vp[e]) << 16);
-              } else {
-                const float* vp = reinterpret_cast<const float*>(vst) + rr * D + dim0;
-#pragma unroll
-                for (int e = 0; e < VEW; ++e) v[u][e] = vp[e];
-              }
-              const int32_t r = s0 + (ok ? rr : 0);
-#pragma unroll
-              for (int hh = 0; hh < G; ++hh) pz[u][hh] = ok ? zs[hh * zcap + r] : 0.0f;
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-              for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-                for (int e = 0; e < VEW; ++e) acc[hh][e] = fmaf(pz[u][hh], v[u][e], acc[hh][e]);
-          }
+          chains(s0, cn - s0 < SR ? cn - s0 : SR);
           bsync();
         }
         return;
@@ -754,11 +826,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
         if (r >= cn || (use_flags && flags[r])) continue;
         float v[VEW];
         cur[u].cvt(v);
+        float pr[G];
+        zrow_load(r, pr);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          const float p = zs[hh * zcap + r];
 #pragma unroll
-          for (int e = 0; e < VEW; ++e) acc[hh][e] = fmaf(p, v[e], acc[hh][e]);
+          for (int e = 0; e < VEW; ++e) acc[hh][e] = fmaf(pr[hh], v[e], acc[hh][e]);
         }
       }
     };
@@ -788,7 +861,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
       bsync();
     } else {
       const int64_t rowbase = bh * a.tree.rows[lv];
-      score_rows(a.tree.NK[lv], rowbase, cm, 0, C, C);
+      score_rows(a.tree.NK[lv], a.tree.NV[lv], rowbase, cm, 0, C, C);
       if (s > 0) {
         if (wid == 0) select_top(C, s, sel_new);
       } else {
@@ -817,7 +890,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     const int64_t rowbase = bh * a.cap;
     for (int64_t c0 = 0; c0 < C0; c0 += zcap) {
       const int32_t cn = static_cast<int32_t>(C0 - c0 < zcap ? C0 - c0 : zcap);
-      score_rows(a.K, rowbase, cm, static_cast<int32_t>(c0), cn, c0 == 0 ? pq : -1);
+      score_rows(a.K, a.V, rowbase, cm, static_cast<int32_t>(c0), cn, c0 == 0 ? pq : -1);
       softmax_pv(a.V, rowbase, cm, static_cast<int32_t>(c0), cn, false);
     }
   }
@@ -863,9 +936,20 @@ template <int D, bool BF16, int G>
 static hipError_t launch_attend_t(const AttnArgs& a, size_t lds, int64_t B, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.n_q * a.Hkv), static_cast<unsigned>(B));
   if (a.n_q * a.Hkv * B < kMultiWaveUnits) {
-    // value rows staged through LDS when it has room (4 waves x 64 lanes x 4 x 16 bytes)
+    // value rows through LDS when it has room: a whole chunk's rows (zcap of them, rounded up
+    // to whole 8-row residue steps -- 8 * 64 / (D / 4) rows -- then to whole 64-lane loads of
+    // 16 bytes), prefetched while the chunk is scored; else rounds of 4 waves x 64 lanes x 4
+    // pieces of 16 bytes
+    constexpr size_t kPiecesPerRow = D * (BF16 ? 2 : 4) / 16;
+    constexpr size_t kStep = 8 * kWave / (D / 4);
+    const size_t rows = (static_cast<size_t>(a.zcap) + kStep - 1) / kStep * kStep;
+    const size_t kFull = (rows * kPiecesPerRow + kWave - 1) / kWave * kWave * 16;
     constexpr size_t kStage = 4 * kWave * 4 * 16;
-    if (lds + kStage <= 65536) {
+    if (lds + kFull <= 65536) {
+      AttnArgs b = a;
+      b.pv_stage = 2;
+      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + kFull, s, b);
+    } else if (lds + kStage <= 65536) {
       AttnArgs b = a;
       b.pv_stage = 1;
       hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + kStage, s, b);

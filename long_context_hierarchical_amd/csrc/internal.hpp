@@ -95,7 +95,8 @@ struct AttnArgs {
   int32_t use_rope;
   int32_t smax;         // capacity of a kept-node list
   int32_t zcap;         // capacity of a scored candidate list (selecting levels and token-level chunks)
-  int32_t pv_stage;     // set by the launcher: several waves per unit stage value rows through LDS
+  int32_t pv_stage;     // set by the launcher, several waves per unit: value rows through LDS in
+                        // rounds (1) or prefetched for a whole chunk while it is scored (2)
   LevelK k;
   TreeLevels tree;
 };
