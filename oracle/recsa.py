@@ -242,6 +242,7 @@ class UnitResult:
     flags: dict = field(default_factory=dict)     # level -> near tie at the selection boundary
     C: dict = field(default_factory=dict)         # level -> candidate count (level 0 included)
     entries: list = field(default_factory=list)   # (level, node or token id) per softmax entry
+    epos: list = field(default_factory=list)      # each entry's index among its level's candidates
     z: np.ndarray | None = None                   # [E, G] float32 logits of the entries
     weights: np.ndarray | None = None             # [E, G] float64 softmax weights
     q_pos: dict = field(default_factory=dict)     # level -> query RoPE position
@@ -295,6 +296,7 @@ def attend_unit(q: np.ndarray, K: np.ndarray, V: np.ndarray, tree, n: int, f: in
         res.sel[lv] = [int(cand[i]) for i in chosen]
         for i in np.sort(order[s:]):
             res.entries.append((lv, int(cand[i])))
+            res.epos.append(int(i))
             zs.append(z[:, i])
             vals.append(NV[cand[i]])
         prev = res.sel[lv]
@@ -310,6 +312,7 @@ def attend_unit(q: np.ndarray, K: np.ndarray, V: np.ndarray, tree, n: int, f: in
         z0 = _logits(q, K[cand0], pq, dtype, theta, scale32)
         for i in range(C0):
             res.entries.append((0, int(cand0[i])))
+            res.epos.append(i)
             zs.append(z0[:, i])
         vals.extend(V[cand0])
     if not zs:

@@ -32,9 +32,10 @@ def rot(x: np.ndarray, p: int, theta: float) -> np.ndarray:
     return np.concatenate([zc.real, zc.imag], axis=-1)
 
 
-def brute_unit(q, K, V, W, n, f, k_levels, theta=1.0e6, scale=None, self_in=False):
+def brute_unit(q, K, V, W, n, f, k_levels, theta=1.0e6, scale=None, self_in=False, fixed_sel=None):
     """Returns dict(out [G,d], lse [G], sel {level: sorted ids}, gap {level: relative boundary gap},
-    entries [(level, id)])."""
+    entries [(level, id)]). fixed_sel {level: kept ids} replaces the selection by scores (the
+    function of q, K, V and W that gradients with held selections differentiate)."""
     q = np.asarray(q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -60,14 +61,19 @@ def brute_unit(q, K, V, W, n, f, k_levels, theta=1.0e6, scale=None, self_in=Fals
             z = np.array([sc * np.dot(rot(q[h], C, theta), rot(key, i, theta)) for h in range(G)])
             zmap[g] = z
             S[g] = z.sum()
-        s = min(int(k_levels[lv - 1]), C)
-        order = sorted(range(C), key=lambda i: (-S[cands[i]], i))
-        if 0 < s < C:
-            mx = max(abs(v) for v in S.values())
-            gap[lv] = (S[cands[order[s - 1]]] - S[cands[order[s]]]) / mx if mx > 0 else 0.0
-        kept = {cands[i] for i in order[:s]}
+        if fixed_sel is not None:
+            kept = set(fixed_sel.get(lv, []))
+            rest = [i for i in range(C) if cands[i] not in kept]
+        else:
+            s = min(int(k_levels[lv - 1]), C)
+            order = sorted(range(C), key=lambda i: (-S[cands[i]], i))
+            if 0 < s < C:
+                mx = max(abs(v) for v in S.values())
+                gap[lv] = (S[cands[order[s - 1]]] - S[cands[order[s]]]) / mx if mx > 0 else 0.0
+            kept = {cands[i] for i in order[:s]}
+            rest = sorted(order[s:])
         sel[lv] = sorted(kept)
-        for i in sorted(order[s:]):
+        for i in rest:
             g = cands[i]
             entries.append((lv, g))
             zs.append(zmap[g])

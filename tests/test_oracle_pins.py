@@ -484,3 +484,87 @@ def test_generate_tree_is_one_shot_tree(dtype):
             assert np.array_equal(k1.view(np.uint32), k2.view(np.uint32))
             assert np.array_equal(v1.view(np.uint32), v2.view(np.uint32))
     assert np.array_equal(from_storage(K, dtype), Ks) and np.array_equal(from_storage(V, dtype), Vs)
+
+
+# ------------------------------------------------------------------ gradients (selections held fixed)
+
+def _bwd_case(seed):
+    rng = np.random.default_rng(3000 + seed)
+    f = [2, 3, 4, 16][seed % 4]
+    d = [8, 16][seed % 2]
+    G = [1, 2, 4][seed % 3]
+    theta = [0.0, 50.0, 1.0e6][(seed // 2) % 3]
+    self_in = bool(seed % 2)
+    n = int(rng.integers(f * f + 1, 200 if f < 16 else 700))
+    k = [int(rng.integers(1, f + 1)) for _ in range(10)]
+    K = _rand(rng, (n, d))
+    V = _rand(rng, (n, d))
+    q = _rand(rng, (G, d))
+    W = (np.eye(d) + 0.3 / np.sqrt(d) * rng.standard_normal((d, d))).astype(np.float32)
+    dout = rng.standard_normal((G, d))
+    dlse = rng.standard_normal(G)
+    return f, d, G, theta, self_in, n, k, K, V, q, W, dout, dlse, rng
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_backward_matches_finite_differences(seed):
+    """Gradients (f32 storage) of F = sum(dout * out) + sum(dlse * lse) with the forward's
+    selections held fixed, against central differences of the independent float64 formulation
+    with those selections, on sampled coordinates of q, K, V and W (through every tree level)."""
+    from oracle.backward import backward
+    f, d, G, theta, self_in, n, k, K, V, q, W, dout, dlse, rng = _bwd_case(seed)
+    kw = dict(q_start=n - 1) if self_in else dict(n_tokens=n)
+    g = backward(K[None, None], V[None, None], W, q[None, None], dout[None, None], f, k, "f32", theta,
+                 dlse=dlse[None, None], **kw)
+    sel = g["results"][(0, 0, 0)].sel
+
+    def F(qx, Kx, Vx, Wx):
+        r = brute_unit(qx, Kx, Vx, Wx, n, f, k, theta, self_in=self_in, fixed_sel=sel)
+        return float(np.sum(dout * r["out"]) + np.sum(dlse * r["lse"]))
+
+    base = [q.astype(np.float64), K.astype(np.float64), V.astype(np.float64), W.astype(np.float64)]
+    grads = [g["dq"][0, 0], g["dK"][0, 0][:n], g["dV"][0, 0][:n], g["dW"]]
+    eps = 1e-6
+    for which in range(4):
+        x = base[which]
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, s)) for s in x.shape)
+            args = [b.copy() for b in base]
+            args[which][idx] += eps
+            fp = F(*args)
+            args[which][idx] -= 2 * eps
+            fm = F(*args)
+            fd = (fp - fm) / (2 * eps)
+            assert abs(fd - grads[which][idx]) <= 2e-5 * (1.0 + abs(fd)), (which, idx, fd, grads[which][idx])
+
+
+def test_backward_without_pruning_is_dense_attention_gradient():
+    """Keeping everything makes each query textbook causal RoPE attention, whose gradients
+    torch's autograd computes in float64 (W gets none: no summary is an entry)."""
+    from oracle.backward import backward
+    rng = np.random.default_rng(11)
+    d, G, n, f, theta = 16, 2, 90, 4, 1.0e4
+    K, V = _rand(rng, (n, d)), _rand(rng, (n, d))
+    q = _rand(rng, (G, d))
+    W = _rand(rng, (d, d), 0.1)
+    dout = rng.standard_normal((G, d))
+    g = backward(K[None, None], V[None, None], W, q[None, None], dout[None, None], f, [INT32_MAX] * 6, "f32",
+                 theta, q_start=n - 1)
+    om = torch.tensor(theta, dtype=torch.float64) ** (-(2.0 * torch.arange(d // 2, dtype=torch.float64)) / d)
+    om = om.to(torch.float32).to(torch.float64)
+
+    def rot(x, p):
+        ang = p[:, None] * om[None, :]
+        c, s = torch.cos(ang), torch.sin(ang)
+        return torch.cat([x[..., :d // 2] * c - x[..., d // 2:] * s, x[..., d // 2:] * c + x[..., :d // 2] * s], -1)
+
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    Kt = torch.tensor(K, dtype=torch.float64, requires_grad=True)
+    Vt = torch.tensor(V, dtype=torch.float64, requires_grad=True)
+    z = rot(qt, torch.full((G,), float(n - 1), dtype=torch.float64)) @ rot(Kt, torch.arange(n, dtype=torch.float64)).T
+    out = torch.softmax(z / np.sqrt(d), dim=-1) @ Vt
+    (out * torch.tensor(dout)).sum().backward()
+    np.testing.assert_allclose(g["dq"][0, 0], qt.grad.numpy(), rtol=0, atol=1e-5)
+    np.testing.assert_allclose(g["dK"][0, 0], Kt.grad.numpy(), rtol=0, atol=1e-5)
+    np.testing.assert_allclose(g["dV"][0, 0], Vt.grad.numpy(), rtol=0, atol=1e-5)
+    assert np.all(g["dW"] == 0.0)
