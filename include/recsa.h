@@ -179,6 +179,42 @@ int32_t recsa_decode_step(const recsa_shape_t* shape, const void* q, const void*
                           float* out, float* lse, int32_t* sel, int32_t sel_width,
                           void* workspace, int64_t ws_bytes, void* stream);
 
+/* Gradients of a recsa_decode (causal = 0) or recsa_prefill (causal = 1) call with respect to
+ * q, K, V and the pooler W [Abstract: RecSA is trained -- its pooler distilled, the model
+ * fine-tuned]. The pages do not say how gradients pass the selection. Reading: which candidates
+ * a level keeps is taken from the forward call's `sel` and held fixed (a discrete choice, not
+ * differentiated), and the forward's roundings to the storage type are passed straight through.
+ * Per query head and entry e (logit z, weight P, value v_e):
+ *   dz = P (dout . v_e - dout . out) + dlse P; v_e gets sum_h P dout_h; the entry's key row gets
+ *   the transposed rotation (at its candidate index) of scale sum_h dz q~_h; q gets the
+ *   transposed rotations (at each level's query position) of scale sum_e dz k~_e.
+ * A node's key is W @ m (m the mean of its children's stored keys), its value the mean of its
+ * children's values: a node's key gradient a adds outer(a, m) to dW and W^T a / f to each
+ * child's key gradient, its value gradient adds 1/f of itself to each child's, level by level
+ * down to the token rows.
+ *   causal = 0: n_q queries at position n_tokens (q_start ignored); causal = 1: query j at
+ *   q_start + j over tokens 0..q_start + j (n_tokens ignored). q, K, V, W, tree, k_per_level
+ *   and n_levels as in the forward call.
+ *   out, lse, sel [dev]: the forward call's outputs (sel is required; sel_width as given there).
+ *   dout [dev]: float32 [B][n_q][H_q][d]; dlse [dev]: float32 [B][n_q][H_q] (nullable: zero).
+ *   dq [dev]: float32 [B][n_q][H_q][d], written.
+ *   dK, dV [dev]: float32 [B][H_kv][capacity][d], and dW [dev]: float32 [d][d], added to (zero
+ *   them before the first call; calls over successive chunks of queries accumulate).
+ *   workspace: recsa_backward_workspace_bytes(shape, n_max, k, n_levels) with n_max = n_tokens
+ *   (decode) or q_start + n_q: the RoPE table and float32 node gradients.
+ * Row gradients are summed with float32 atomic adds, in an order the hardware chooses, so they
+ * are not bitwise reproducible from run to run.
+ * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED, WORKSPACE. */
+int64_t recsa_backward_workspace_bytes(const recsa_shape_t* shape, int64_t n_max,
+                                       const int32_t* k_per_level, int32_t n_levels);
+int32_t recsa_backward(const recsa_shape_t* shape, int32_t causal, const void* q, int64_t q_start,
+                       int64_t n_q, int64_t n_tokens, const void* K, const void* V, const void* W,
+                       const void* tree, const int32_t* k_per_level, int32_t n_levels,
+                       const float* out, const float* lse, const int32_t* sel, int32_t sel_width,
+                       const float* dout, const float* dlse,
+                       float* dq, float* dK, float* dV, float* dW,
+                       void* workspace, int64_t ws_bytes, void* stream);
+
 /* Dense softmax attention with standard RoPE at the original positions -- the comparator the
  * method is timed against [Abstract]; also RecSA's limit when every level keeps everything.
  * mode: RECSA_DENSE_CAUSAL (bit 0) and/or RECSA_DENSE_KEYS_ROTATED (bit 1).

@@ -449,6 +449,138 @@ int32_t recsa_decode_step(const recsa_shape_t* shape, const void* q, const void*
   return launch_planned_attend(pl, st);
 }
 
+// Gradient workspace: the RoPE table, then float32 node-key and node-value gradients laid out
+// like the tree (levels 1..T(capacity), keys then values per level).
+static int64_t grad_level_offset(const Info& I, int lv, int which) {
+  Info J = I;
+  J.esz = 4;
+  return level_offset_bytes(J, lv, which);
+}
+
+static int32_t backward_bounds(const Info& I, int64_t n_max, const int32_t* k, int32_t n_levels, Bounds* bd) {
+  int32_t rc = check_k(k, n_levels, levels_of(n_max, I.f));
+  if (rc) return rc;
+  *bd = bounds_for(I, n_max, k);
+  if (bd->smax > kMaxList || bd->csel > kMaxList)
+    return fail(RECSA_ERR_UNSUPPORTED, "candidate lists up to %lld entries exceed %lld",
+                (long long)std::max(bd->smax, bd->csel), (long long)kMaxList);
+  return RECSA_OK;
+}
+
+int64_t recsa_backward_workspace_bytes(const recsa_shape_t* shape, int64_t n_max, const int32_t* k, int32_t n_levels) {
+  Info I;
+  if (check_shape(shape, &I)) return -1;
+  if (n_max < 0) {
+    fail(RECSA_ERR_INVALID_ARG, "n_max must be >= 0");
+    return -1;
+  }
+  Bounds bd;
+  if (backward_bounds(I, n_max, k, n_levels, &bd)) return -1;
+  return table_bytes(I, bd.P) + grad_level_offset(I, levels_of(I.cap, I.f) + 1, 0);
+}
+
+int32_t recsa_backward(const recsa_shape_t* shape, int32_t causal, const void* q, int64_t q_start, int64_t n_q,
+                       int64_t n_tokens, const void* K, const void* V, const void* W, const void* tree,
+                       const int32_t* k, int32_t n_levels, const float* out, const float* lse, const int32_t* sel,
+                       int32_t sel_width, const float* dout, const float* dlse, float* dq, float* dK, float* dV,
+                       float* dW, void* workspace, int64_t ws_bytes, void* stream) {
+  Info I;
+  int32_t rc = check_shape(shape, &I);
+  if (rc) return rc;
+  if (causal != 0 && causal != 1) return fail(RECSA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (n_q < 0) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 0");
+  if (n_q * I.Hkv > INT32_MAX || I.B > 65535) return fail(RECSA_ERR_UNSUPPORTED, "grid too large");
+  if (causal && q_start < 0) return fail(RECSA_ERR_INVALID_ARG, "q_start must be >= 0");
+  if (!causal && n_tokens < 0) return fail(RECSA_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  const int64_t n_max = causal ? q_start + n_q : n_tokens;
+  const int64_t n_min = causal ? q_start + 1 : n_tokens;
+  if (n_max > I.cap)
+    return fail(RECSA_ERR_CAPACITY, "%lld tokens exceed the capacity %lld", (long long)n_max, (long long)I.cap);
+  Bounds bd;
+  rc = backward_bounds(I, n_max, k, n_levels, &bd);
+  if (rc) return rc;
+  if (n_q == 0) return RECSA_OK;
+  const int T = levels_of(n_max, I.f);
+  if (!q || !out || !lse || !sel || !dout || !dq || !dK || !dV || !dW || (n_max > 0 && (!K || !V)) ||
+      (T > 0 && (!tree || !W)))
+    return fail(RECSA_ERR_INVALID_ARG, "q, K, V, W, tree, out, lse, sel, dout, dq, dK, dV or dW is NULL");
+  if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(tree) || !aligned16(out) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dK) || !aligned16(dV) || !aligned16(dW) || !aligned16(workspace))
+    return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  int32_t need = 0;
+  for (int64_t n = n_min; n <= n_max; ++n) need = std::max(need, max_kept(n, I.f, k));
+  if (sel_width < std::max(need, 1)) return fail(RECSA_ERR_INVALID_ARG, "sel_width %d < %d kept nodes", sel_width, need);
+  const int64_t tab = table_bytes(I, bd.P);
+  const int64_t need_ws = tab + grad_level_offset(I, levels_of(I.cap, I.f) + 1, 0);
+  if (ws_bytes < need_ws) return fail(RECSA_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes, (long long)need_ws);
+  if (!workspace) return fail(RECSA_ERR_INVALID_ARG, "workspace is NULL");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = fill_table(I, bd.P, workspace, st);
+  if (rc) return rc;
+  char* gbase = static_cast<char*>(workspace) + tab;
+  const int Tc = levels_of(I.cap, I.f);
+  for (int lv = 1; lv <= T; ++lv) {
+    hipError_t e = recsa::launch_fill_zero(reinterpret_cast<float*>(gbase + grad_level_offset(I, lv, 0)),
+                                           2 * I.B * I.Hkv * nodes_at(I.cap, I.f, lv) * I.d, st);
+    if (e != hipSuccess) return hip_fail(e, "gradient workspace clear");
+  }
+  recsa::BwdArgs a{};
+  a.q = q;
+  a.K = K;
+  a.V = V;
+  a.out = out;
+  a.lse = lse;
+  a.sel = sel;
+  a.dout = dout;
+  a.dlse = dlse;
+  a.dq = dq;
+  a.dK = dK;
+  a.dV = dV;
+  a.tab = static_cast<const float2*>(workspace);
+  a.cap = I.cap;
+  a.n_q = n_q;
+  a.n_fixed = n_tokens;
+  a.q_start = causal ? q_start : 0;
+  a.causal = causal;
+  a.Hkv = static_cast<int32_t>(I.Hkv);
+  a.Hq = static_cast<int32_t>(I.Hq);
+  a.f = static_cast<int32_t>(I.f);
+  a.n_levels = n_levels;
+  a.sel_width = sel_width;
+  a.scale = I.scale;
+  a.use_rope = I.theta != 0.0f;
+  a.zcap = static_cast<int32_t>((bd.csel + 15) / 16 * 16);
+  a.smax = static_cast<int32_t>(bd.smax);
+  for (int lv = 1; lv <= Tc && lv <= RECSA_MAX_LEVELS; ++lv) {
+    a.tree.NK[lv] = static_cast<const char*>(tree) + level_offset_bytes(I, lv, 0);
+    a.tree.NV[lv] = static_cast<const char*>(tree) + level_offset_bytes(I, lv, 1);
+    a.tree.rows[lv] = nodes_at(I.cap, I.f, lv);
+    a.gNK[lv] = reinterpret_cast<float*>(gbase + grad_level_offset(I, lv, 0));
+    a.gNV[lv] = reinterpret_cast<float*>(gbase + grad_level_offset(I, lv, 1));
+  }
+  hipError_t e = recsa::launch_backward_units(a, static_cast<int>(I.d), I.bf16, static_cast<int>(I.G), I.B, st);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  for (int lv = T; lv >= 1; --lv) {
+    recsa::TreePushArgs p{};
+    p.childK = lv == 1 ? K : a.tree.NK[lv - 1];
+    p.child_rows = lv == 1 ? I.cap : nodes_at(I.cap, I.f, lv - 1);
+    p.gk = a.gNK[lv];
+    p.gv = a.gNV[lv];
+    p.rows = nodes_at(I.cap, I.f, lv);
+    p.n_nodes = nodes_at(n_max, I.f, lv);
+    p.ck = lv == 1 ? dK : a.gNK[lv - 1];
+    p.cv = lv == 1 ? dV : a.gNV[lv - 1];
+    p.W = W;
+    p.dW = dW;
+    p.f = static_cast<int32_t>(I.f);
+    p.BH = static_cast<int32_t>(I.B * I.Hkv);
+    e = recsa::launch_tree_push(p, static_cast<int>(I.d), I.bf16, st);
+    if (e != hipSuccess) return hip_fail(e, "tree gradient launch");
+  }
+  return RECSA_OK;
+}
+
 struct DensePlan {
   int64_t kr_bytes = 0, part_o_bytes = 0, part_ml_bytes = 0, total = 0, keys_per_split = 0;
   int32_t splits = 1;

@@ -103,6 +103,58 @@ struct AttnArgs {
 
 size_t attend_lds_bytes(int d, int G, int smax, int zcap);
 
+// ---------------------------------------------------------------- gradients (selections held fixed)
+struct BwdArgs {
+  const void* q;        // [B][n_q][H_q][d] storage type
+  const void* K;        // [B*H_kv][cap][d]
+  const void* V;
+  const float* out;     // forward outputs [B][n_q][H_q][d]
+  const float* lse;     // forward log-sum-exp [B][n_q][H_q]
+  const int32_t* sel;   // forward selections [B][n_q][H_kv][n_levels][sel_width]
+  const float* dout;    // [B][n_q][H_q][d]
+  const float* dlse;    // [B][n_q][H_q] or null
+  float* dq;            // [B][n_q][H_q][d] (written)
+  float* dK;            // [B*H_kv][cap][d] (added to)
+  float* dV;
+  const float2* tab;    // RoPE table, rows 0..P
+  int64_t cap;
+  int64_t n_q;
+  int64_t n_fixed;      // decode: visible tokens
+  int64_t q_start;      // causal: position of query 0
+  int32_t causal;
+  int32_t Hkv, Hq, f;
+  int32_t n_levels, sel_width;
+  float scale;
+  int32_t use_rope;
+  int32_t zcap;         // capacity of the kept-flag list
+  int32_t smax;         // capacity of the kept-parent list
+  TreeLevels tree;      // forward node rows
+  float* gNK[RECSA_MAX_LEVELS + 1];   // node-key gradients, [B*H_kv][rows[l]][d] (added to)
+  float* gNV[RECSA_MAX_LEVELS + 1];
+};
+size_t backward_unit_lds_bytes(int zcap, int smax);
+hipError_t launch_backward_units(const BwdArgs& a, int d, bool bf16, int G, int64_t B, hipStream_t s);
+
+// One level of the top-down push: every node of level `level` with a nonzero gradient adds
+// outer(dkey, m) to dW, W^T dkey / f to each child's key gradient and dvalue / f to each
+// child's value gradient (children: token rows at level 1, level-(l-1) nodes above).
+struct TreePushArgs {
+  const void* childK;   // stored child keys [BH][child_rows][d] (token rows or level l-1 nodes)
+  int64_t child_rows;
+  const float* gk;      // this level's node gradients [BH][rows][d]
+  const float* gv;
+  int64_t rows;
+  int64_t n_nodes;      // nodes of this level per slice
+  float* ck;            // child gradients [BH][child_rows][d] (added to)
+  float* cv;
+  const void* W;        // [d][d]
+  float* dW;            // [d][d] (added to)
+  int32_t f;
+  int32_t BH;
+};
+hipError_t launch_tree_push(const TreePushArgs& a, int d, bool bf16, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+
 // ---------------------------------------------------------------- dense reference attention
 // Keys rotated at their own positions: Kr[bh][p] = round(rot(K[bh][p], p)), p < n
 // (K rows per slice: cap; Kr rows per slice: kr_rows).

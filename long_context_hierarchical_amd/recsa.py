@@ -21,7 +21,7 @@ INT32_MAX = 2 ** 31 - 1
 EXPORTS = (
     "recsa_abi_version", "recsa_last_error", "recsa_num_levels", "recsa_tree_bytes", "recsa_level_offset",
     "recsa_sel_width", "recsa_workspace_bytes", "recsa_build_tree", "recsa_decode", "recsa_prefill",
-    "recsa_decode_step",
+    "recsa_decode_step", "recsa_backward_workspace_bytes", "recsa_backward",
     "recsa_dense_workspace_bytes", "recsa_dense_ref_attn", "recsa_rotate_keys",
 )
 RECSA_DENSE_CAUSAL, RECSA_DENSE_KEYS_ROTATED = 1, 2
@@ -87,6 +87,9 @@ def lib() -> ctypes.CDLL:
             "recsa_decode": (I32, [SP, P, I64, P, P, P, I64, K, I32, P, P, P, I32, P, I64, P]),
             "recsa_prefill": (I32, [SP, P, I64, I64, P, P, P, K, I32, P, P, P, I32, P, I64, P]),
             "recsa_decode_step": (I32, [SP, P, P, P, P, P, P, P, I64, K, I32, P, P, P, I32, P, I64, P]),
+            "recsa_backward_workspace_bytes": (I64, [SP, I64, K, I32]),
+            "recsa_backward": (I32, [SP, I32, P, I64, I64, I64, P, P, P, P, K, I32, P, P, P, I32, P, P, P, P, P, P,
+                                     P, I64, P]),
             "recsa_dense_workspace_bytes": (I64, [SP, I64, I64, I32]),
             "recsa_dense_ref_attn": (I32, [SP, P, I64, I64, P, P, I64, I32, P, P, P, I64, P]),
             "recsa_rotate_keys": (I32, [SP, P, I64, P, P]),
@@ -152,6 +155,11 @@ def recsa_workspace_bytes(shape: Shape, n_max: int, k_levels) -> int:
     return _nbytes(lib().recsa_workspace_bytes(ctypes.byref(shape.c()), n_max, k, nl))
 
 
+def recsa_backward_workspace_bytes(shape: Shape, n_max: int, k_levels) -> int:
+    k, nl = _k(k_levels)
+    return _nbytes(lib().recsa_backward_workspace_bytes(ctypes.byref(shape.c()), n_max, k, nl))
+
+
 def recsa_dense_workspace_bytes(shape: Shape, n_tokens: int, n_q: int, mode: int) -> int:
     return _nbytes(lib().recsa_dense_workspace_bytes(ctypes.byref(shape.c()), n_tokens, n_q, mode))
 
@@ -188,6 +196,17 @@ def recsa_decode_step(shape: Shape, q, k_new, v_new, K, V, W, tree, n_tokens: in
     _check(lib().recsa_decode_step(ctypes.byref(shape.c()), _p(q), _p(k_new), _p(v_new), _p(K), _p(V), _p(W),
                                    _p(tree), n_tokens, k, nl, _p(out), _p(lse), _p(sel), sel_width,
                                    _p(workspace), ws_bytes, _stream(stream)))
+
+
+def recsa_backward(shape: Shape, causal: bool, q, q_start: int, n_tokens: int, K, V, W, tree, k_levels, out, lse,
+                   sel, sel_width: int, dout, dq, dK, dV, dW, dlse=None, workspace=None, stream=None):
+    k, nl = _k(k_levels)
+    n_q = q.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().recsa_backward(ctypes.byref(shape.c()), 1 if causal else 0, _p(q), q_start, n_q, n_tokens, _p(K),
+                                _p(V), _p(W), _p(tree), k, nl, _p(out), _p(lse), _p(sel), sel_width, _p(dout),
+                                _p(dlse), _p(dq), _p(dK), _p(dV), _p(dW), _p(workspace), ws_bytes,
+                                _stream(stream)))
 
 
 def recsa_dense_ref_attn(shape: Shape, q, q_start: int, K, V, n_tokens: int, mode: int, out, lse=None,

@@ -136,3 +136,15 @@ def test_error_paths_return_status_before_launch():
     assert _status(step, sh, q1, kn, kn, t, t, t, t, 4095, [8, 8], t, workspace=t, stream=ns) == -1
     assert _status(step, sh, q1, kn, kn, t, t, t, t, 100, k, t, None, None, 0, small_ws, stream=ns) == -5
     assert _status(step, sh, q1, kn, kn, t, t, t, t, 100, k, t, None, t, 0, t, stream=ns) == -1  # sel_width
+    # gradients: mode, capacity, the forward's selections, their width and the workspace are checked first
+    bwd = R.recsa_backward
+    w8 = R.recsa_sel_width(sh, 4096, 4096, k)
+    args = (t, t, t, t, k, t, t, t, w8, t, t, t, t, t)
+    assert _status(bwd, sh, False, q, 0, 5000, *args, workspace=t, stream=ns) == -2
+    assert _status(bwd, sh, True, q, 4094, 0, *args, workspace=t, stream=ns) == -2
+    assert _status(bwd, sh, False, q, 0, 4096, t, t, t, t, k, t, t, None, w8, t, t, t, t, t, workspace=t,
+                   stream=ns) == -1
+    assert _status(bwd, sh, False, q, 0, 4096, t, t, t, t, k, t, t, t, 1, t, t, t, t, t, workspace=t,
+                   stream=ns) == -1
+    assert _status(bwd, sh, False, q, 0, 4096, *args, workspace=small_ws, stream=ns) == -5
+    assert R.recsa_backward_workspace_bytes(sh, 4096, k) > R.recsa_workspace_bytes(sh, 4096, k)
