@@ -328,55 +328,76 @@ hipError_t launch_backward_units(const BwdArgs& a, int d, bool bf16, int G, int6
 
 // ---------------------------------------------------------------- top-down push
 
-// One level: tiles of NB nodes per workgroup iteration (grid-stride over tiles, y = slice).
-// Thread layout for dW: thread t owns row t / TPR, columns (t % TPR) * CPT .. + CPT, summed over
-// the tiles it sees and added to dW once at the end. For W^T dkey: thread t computes output
-// i = t % D for NB / (256 / D) nodes. Nodes whose key and value gradients are both 0 are skipped.
+// One level. Persistent workgroups take tiles of NB nodes of one slice in turn (the grid strides
+// over (slice, tile) pairs). Per tile: the nodes' key gradients a go to LDS (a node whose key
+// and value gradients are both 0 is skipped); each thread sums one 16-byte piece of one node's
+// children in child order and divides by f (the forward's m); thread t adds
+// sum_nodes a[t / TPR] * m[...] into its CPT entries of row t / TPR of dW; W^T a comes from W
+// in LDS (bf16 storage; float32 W is read through the cache); then each thread adds its
+// 4-float pieces of W^T a / f and of the value gradient / f to every child, as float4
+// read-modify-writes (a child has one parent, so nothing else writes it in this launch).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void tree_push_kernel(TreePushArgs a) {
   constexpr int NT = 256, NB = 16;
   constexpr int TPR = NT / D, CPT = D / TPR;     // dW: threads per row, columns per thread
-  constexpr int NPG = NB / TPR;                  // W^T dkey: nodes per thread
-  __shared__ float ag[NB][D], bg[NB][D], mg[NB][D];
+  constexpr int NPG = NB / TPR;                  // W^T a: nodes per thread
+  constexpr int EPC = 8;                         // elements per child piece (16 bytes of bf16)
+  constexpr int PPR = D / EPC;                   // pieces per row
+  constexpr int Q4 = D / 4;                      // float4 pieces per row
+  __shared__ uint16_t Ws[BF16 ? D * D : 1];
+  __shared__ float ag[NB][D], mg[NB][D], dmg[NB][D];
   __shared__ int touched[NB];
   const int tid = threadIdx.x;
-  const int64_t slice = blockIdx.y;
   const int f = a.f;
   const float ff = static_cast<float>(f);
   const bool pow2 = (f & (f - 1)) == 0;
   const float inv_f = 1.0f / ff;
+  if constexpr (BF16) {
+    for (int i = tid; i < D * D / 8; i += NT)
+      reinterpret_cast<uint4*>(Ws)[i] = reinterpret_cast<const uint4*>(a.W)[i];
+  }
   const int wr = tid / TPR, wc0 = (tid % TPR) * CPT;
   float dw[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) dw[c] = 0.0f;
-  const int64_t ntiles = (a.n_nodes + NB - 1) / NB;
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  const int64_t tiles = (a.n_nodes + NB - 1) / NB;
+  for (int64_t job = blockIdx.x; job < tiles * a.BH; job += gridDim.x) {
+    const int64_t slice = job / tiles, tile = job % tiles;
+    const int64_t g0 = tile * NB;
     if (tid < NB) touched[tid] = 0;
     __syncthreads();
-    for (int idx = tid; idx < NB * D; idx += NT) {
-      const int nd = idx / D, e = idx % D;
-      const int64_t g = tile * NB + nd;
-      float va = 0.0f, vb = 0.0f;
-      if (g < a.n_nodes) {
-        va = a.gk[(slice * a.rows + g) * D + e];
-        vb = a.gv[(slice * a.rows + g) * D + e];
+    for (int idx = tid; idx < NB * Q4; idx += NT) {
+      const int nd = idx / Q4, q = idx % Q4;
+      float4 va = make_float4(0.0f, 0.0f, 0.0f, 0.0f), vb = va;
+      if (g0 + nd < a.n_nodes) {
+        va = reinterpret_cast<const float4*>(a.gk + (slice * a.rows + g0 + nd) * D)[q];
+        vb = reinterpret_cast<const float4*>(a.gv + (slice * a.rows + g0 + nd) * D)[q];
       }
-      ag[nd][e] = va;
-      bg[nd][e] = vb;
-      if (va != 0.0f || vb != 0.0f) touched[nd] = 1;
+      reinterpret_cast<float4*>(ag[nd])[q] = va;
+      if (va.x != 0.0f || va.y != 0.0f || va.z != 0.0f || va.w != 0.0f || vb.x != 0.0f || vb.y != 0.0f ||
+          vb.z != 0.0f || vb.w != 0.0f)
+        touched[nd] = 1;
     }
     __syncthreads();
     // m: the forward's mean of the children's stored keys (child order, float32, / f)
-    for (int idx = tid; idx < NB * D; idx += NT) {
-      const int nd = idx / D, e = idx % D;
-      float m = 0.0f;
+    for (int idx = tid; idx < NB * PPR; idx += NT) {
+      const int nd = idx / PPR, pc = idx % PPR;
+      float m[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) m[e] = 0.0f;
       if (touched[nd]) {
-        const int64_t g = tile * NB + nd;
-        float acc = 0.0f;
-        for (int c = 0; c < f; ++c) acc = acc + load1<BF16>(a.childK, (slice * a.child_rows + g * f + c) * D + e);
-        m = pow2 ? acc * inv_f : acc / ff;
+        const int64_t cbase = (slice * a.child_rows + (g0 + nd) * f) * D + pc * EPC;
+        for (int c = 0; c < f; ++c) {
+          float x[EPC];
+          load8<BF16>(a.childK, cbase + static_cast<int64_t>(c) * D, x);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) m[e] = m[e] + x[e];
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) m[e] = pow2 ? m[e] * inv_f : m[e] / ff;
       }
-      mg[nd][e] = m;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) mg[nd][pc * EPC + e] = m[e];
     }
     __syncthreads();
 #pragma unroll 1
@@ -393,21 +414,29 @@ __global__ __launch_bounds__(256) void tree_push_kernel(TreePushArgs a) {
       for (int u = 0; u < NPG; ++u) dm[u] = 0.0f;
 #pragma unroll 4
       for (int k = 0; k < D; ++k) {
-        const float w = load1<BF16>(a.W, static_cast<int64_t>(k) * D + i);
+        float w;
+        if constexpr (BF16) w = __uint_as_float(static_cast<uint32_t>(Ws[k * D + i]) << 16);
+        else w = static_cast<const float*>(a.W)[static_cast<int64_t>(k) * D + i];
 #pragma unroll
         for (int u = 0; u < NPG; ++u) dm[u] = fmaf(w, ag[nd0 + u][k], dm[u]);
       }
 #pragma unroll
-      for (int u = 0; u < NPG; ++u) {
-        const int nd = nd0 + u;
-        if (!touched[nd]) continue;
-        const int64_t g = tile * NB + nd;
-        const float dk = dm[u] / ff, dv = bg[nd][i] / ff;
-        for (int c = 0; c < f; ++c) {
-          const int64_t o = (slice * a.child_rows + g * f + c) * D + i;
-          a.ck[o] += dk;
-          a.cv[o] += dv;
-        }
+      for (int u = 0; u < NPG; ++u) dmg[nd0 + u][i] = dm[u] / ff;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < NB * Q4; idx += NT) {
+      const int nd = idx / Q4, q = idx % Q4;
+      if (!touched[nd]) continue;
+      const float4 dk = reinterpret_cast<const float4*>(dmg[nd])[q];
+      float4 dv = reinterpret_cast<const float4*>(a.gv + (slice * a.rows + g0 + nd) * D)[q];
+      dv = make_float4(dv.x / ff, dv.y / ff, dv.z / ff, dv.w / ff);
+      const int64_t cbase = (slice * a.child_rows + (g0 + nd) * f) * D;
+      for (int c = 0; c < f; ++c) {
+        float4* pk = reinterpret_cast<float4*>(a.ck + cbase + static_cast<int64_t>(c) * D) + q;
+        float4* pv = reinterpret_cast<float4*>(a.cv + cbase + static_cast<int64_t>(c) * D) + q;
+        const float4 ok = *pk, ov = *pv;
+        *pk = make_float4(ok.x + dk.x, ok.y + dk.y, ok.z + dk.z, ok.w + dk.w);
+        *pv = make_float4(ov.x + dv.x, ov.y + dv.y, ov.z + dv.z, ov.w + dv.w);
       }
     }
     __syncthreads();
@@ -417,13 +446,24 @@ __global__ __launch_bounds__(256) void tree_push_kernel(TreePushArgs a) {
     if (dw[c] != 0.0f) unsafeAtomicAdd(a.dW + static_cast<int64_t>(wr) * D + wc0 + c, dw[c]);
 }
 
+static int push_grid() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return 2 * cus;
+}
+
 template <int D, bool BF16>
 static hipError_t launch_push_t(const TreePushArgs& a, hipStream_t s) {
   if (a.n_nodes <= 0 || a.BH <= 0) return hipSuccess;
-  const int64_t ntiles = (a.n_nodes + 15) / 16;
-  const int64_t gx = ntiles < 256 ? ntiles : 256;
-  hipLaunchKernelGGL((tree_push_kernel<D, BF16>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(a.BH)), dim3(256),
-                     0, s, a);
+  const int64_t jobs = (a.n_nodes + 15) / 16 * a.BH;
+  const int64_t g = jobs < push_grid() ? jobs : push_grid();
+  hipLaunchKernelGGL((tree_push_kernel<D, BF16>), dim3(static_cast<unsigned>(g)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
