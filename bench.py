@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--no-library-legs", action="store_true",
                     help="skip the library flash-attention comparison (torch scaled_dot_product_attention)")
     ap.add_argument("--no-legs", action="store_true", help="skip the dense and prefill comparison legs")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the gradients")
     ap.add_argument("--prefill-chunk", type=int, default=4096)
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step benchmark, sweep the context length (decode 4K-2M, chunked "
@@ -462,7 +463,7 @@ def main():
     kinfo = {
         "pool_kernel": dict(bytes=bb / build_launches, ms=build_ms / build_launches,
                             src=kernel_hash("build_tree.hip", "common.hpp")),
-        "attend_kernel": dict(bytes=db, ms=decode_ms, src=kernel_hash("attend.hip", "common.hpp")),
+        "attend_kernel": dict(bytes=db, ms=decode_ms, src=kernel_hash("attend.hip", "common.hpp", "lanes.hpp")),
     }
     dom = "pool_kernel" if build_ms >= decode_ms else "attend_kernel"
 
@@ -594,6 +595,82 @@ def main():
         per = e0.elapsed_time(e1) / n_calls
         res["breakdown"]["step_mode"] = {"ms_per_call": round(per, 4), "queries_per_call": w.B,
                                          "queries_per_s": round(w.B / (per * 1e-3), 1)}
+
+        # autoregressive decoding: the cache's last S positions generated again, one
+        # recsa_decode_step per token (append, build what completes, attend with the own token).
+        # Re-appending a cached token rebuilds its completed nodes bit for bit, so the work per
+        # step is exactly that of generating at that position.
+        S = min(256, w.n_queries)
+        n0 = w.L - S
+        kn = K[:, :, n0:].permute(2, 0, 1, 3).contiguous()
+        vn = V[:, :, n0:].permute(2, 0, 1, 3).contiguous()
+        qs = q[:, :S].transpose(0, 1).contiguous()
+        gout = torch.empty(S, w.B, w.Hq, w.d, dtype=torch.float32, device=dev)
+
+        def generate():
+            for s in range(S):
+                R.recsa_decode_step(sh, qs[s], kn[s], vn[s], K, V, W, tree, n0 + s, k, gout[s], None, None, 0, ws)
+
+        def generate_unfused():
+            for s in range(S):
+                t = n0 + s
+                K[:, :, t].copy_(kn[s])
+                V[:, :, t].copy_(vn[s])
+                R.recsa_build_tree(sh, K, V, W, t, t + 1, tree)
+                R.recsa_prefill(sh, qs[s].unsqueeze(1), t, K, V, tree, k, gout[s].unsqueeze(1), None, None, 0, ws)
+
+        gen = {"positions": [n0, w.L], "tokens_per_step": w.B}
+        for name, fn in (("fused", generate), ("unfused", generate_unfused)):
+            fn()
+            torch.cuda.synchronize()
+            h0 = time.perf_counter()
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            host = (time.perf_counter() - h0) * 1e3 / S
+            per = e0.elapsed_time(e1) / S
+            gen[name] = {"ms_per_step": round(per, 4), "tokens_per_s": round(w.B / (per * 1e-3), 1),
+                         "host_ms_per_step": round(host, 4)}
+        res["breakdown"]["generation"] = gen
+        del kn, vn, qs, gout
+
+    if not args.no_backward:
+        # gradients with the forward's selections held fixed: the batched decode's 1024 queries,
+        # and causal prefill of the last 4096 positions of each sequence
+        log("gradients: batched decode, prefill chunk")
+        bwd = {}
+        bws = torch.zeros(R.recsa_backward_workspace_bytes(sh, w.L, k), dtype=torch.uint8, device=dev)
+        dK = torch.zeros(w.B, w.Hkv, w.L, w.d, dtype=torch.float32, device=dev)
+        dV = torch.zeros_like(dK)
+        dW = torch.zeros(w.d, w.d, dtype=torch.float32, device=dev)
+        R.recsa_decode(sh, q, K, V, tree, w.L, k, out, lse, sel, width, ws)
+        dout = torch.randn(out.shape, device=dev, generator=torch.Generator(device=dev).manual_seed(5))
+        dq = torch.empty_like(out)
+        ms = timed(lambda: R.recsa_backward(sh, False, q, 0, w.L, K, V, W, tree, k, out, lse, sel, width, dout, dq, dK,
+                                            dV, dW, workspace=bws), 3)
+        bwd["decode_batched"] = {"ms_per_call": round(ms, 4), "queries_per_call": n_queries,
+                                 "queries_per_s": round(n_queries / (ms * 1e-3), 1),
+                                 "forward_ms": round(decode_ms, 4)}
+        c = args.prefill_chunk
+        from synthetic import with_overrides as _wo
+        wq = _wo(w, seed=w.seed + 1000)
+        qc = torch.empty(w.B, c, w.Hq, w.d, dtype=td, device=dev)
+        for b in range(w.B):
+            qc[b] = up(gen_queries(wq, b, c))
+        csw = R.recsa_sel_width(sh, w.L - c + 1, w.L, k)
+        cout = torch.empty(w.B, c, w.Hq, w.d, dtype=torch.float32, device=dev)
+        clse = torch.empty(w.B, c, w.Hq, dtype=torch.float32, device=dev)
+        csel = torch.empty(w.B, c, w.Hkv, len(k), csw, dtype=torch.int32, device=dev)
+        fwd_ms = timed(lambda: R.recsa_prefill(sh, qc, w.L - c, K, V, tree, k, cout, clse, csel, csw, ws), 3)
+        cdout = torch.randn(cout.shape, device=dev, generator=torch.Generator(device=dev).manual_seed(6))
+        cdq = torch.empty_like(cout)
+        ms = timed(lambda: R.recsa_backward(sh, True, qc, w.L - c, 0, K, V, W, tree, k, cout, clse, csel, csw, cdout, cdq,
+                                            dK, dV, dW, workspace=bws), 2)
+        bwd["prefill_last_chunk"] = {"ms_per_call": round(ms, 4), "tokens_per_call": w.B * c,
+                                     "tokens_per_s": round(w.B * c / (ms * 1e-3), 1), "forward_ms": round(fwd_ms, 4)}
+        res["breakdown"]["backward"] = bwd
+        del bws, dK, dV, dW, dout, dq, qc, cout, clse, csel, cdout, cdq
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
