@@ -582,7 +582,7 @@ int32_t recsa_backward(const recsa_shape_t* shape, int32_t causal, const void* q
 }
 
 struct DensePlan {
-  int64_t kr_bytes = 0, part_o_bytes = 0, part_ml_bytes = 0, total = 0, keys_per_split = 0;
+  int64_t kr_bytes = 0, qr_bytes = 0, part_o_bytes = 0, part_ml_bytes = 0, total = 0, keys_per_split = 0;
   int32_t splits = 1;
 };
 
@@ -591,6 +591,8 @@ static DensePlan dense_plan(const Info& I, int64_t n_tokens, int64_t n_q, int32_
   const bool causal = mode & RECSA_DENSE_CAUSAL;
   const bool rotated = mode & RECSA_DENSE_KEYS_ROTATED;
   if (!rotated && I.theta != 0.0f) p.kr_bytes = ((I.B * I.Hkv * n_tokens * I.d * I.esz) + 255) / 256 * 256;
+  // bf16 runs on the matrix cores with the queries rotated beforehand
+  if (I.bf16 && I.theta != 0.0f) p.qr_bytes = ((I.B * n_q * I.Hq * I.d * 2) + 255) / 256 * 256;
   p.keys_per_split = std::max<int64_t>(n_tokens, 1);
   if (I.bf16 && !causal && n_tokens > 0 && n_q > 0) {
     const int64_t qpb = recsa::dense_queries_per_block(static_cast<int>(I.G));
@@ -608,7 +610,7 @@ static DensePlan dense_plan(const Info& I, int64_t n_tokens, int64_t n_q, int32_
     p.part_o_bytes = (rows * I.d * 4 + 255) / 256 * 256;
     p.part_ml_bytes = (rows * 2 * 4 + 255) / 256 * 256;
   }
-  p.total = p.kr_bytes + p.part_o_bytes + p.part_ml_bytes;
+  p.total = p.kr_bytes + p.qr_bytes + p.part_o_bytes + p.part_ml_bytes;
   return p;
 }
 
@@ -703,8 +705,14 @@ int32_t recsa_dense_ref_attn(const recsa_shape_t* shape, const void* q, int64_t 
     a.kr_rows = n_tokens;
   }
   if (pl.splits > 1) {
-    a.part_o = reinterpret_cast<float*>(ws + pl.kr_bytes);
-    a.part_ml = reinterpret_cast<float*>(ws + pl.kr_bytes + pl.part_o_bytes);
+    a.part_o = reinterpret_cast<float*>(ws + pl.kr_bytes + pl.qr_bytes);
+    a.part_ml = reinterpret_cast<float*>(ws + pl.kr_bytes + pl.qr_bytes + pl.part_o_bytes);
+  }
+  if (pl.qr_bytes > 0) {
+    hipError_t e = recsa::launch_rotate_queries(a, ws + pl.kr_bytes, I.B, static_cast<int>(I.d), st);
+    if (e != hipSuccess) return hip_fail(e, "query rotation launch");
+    a.q = ws + pl.kr_bytes;
+    a.use_rope = 0;   // the keys and now the queries are rotated
   }
   hipError_t e = recsa::launch_dense(a, static_cast<int>(I.d), I.bf16, static_cast<int>(I.G), I.B, st);
   if (e != hipSuccess) return hip_fail(e, "dense attention launch");

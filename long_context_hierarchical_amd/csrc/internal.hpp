@@ -182,6 +182,8 @@ struct DenseArgs {
 // Query rows per workgroup of the dense kernel (G query heads of one KV head per query).
 int dense_queries_per_block(int G);
 hipError_t launch_dense(const DenseArgs& a, int d, bool bf16, int G, int64_t B, hipStream_t s);
+// bf16 queries rotated at their positions into qr ([B][n_q][H_q][d], bf16), for the MFMA kernel.
+hipError_t launch_rotate_queries(const DenseArgs& a, void* qr, int64_t B, int d, hipStream_t s);
 hipError_t launch_attend(const AttnArgs& a, int d, bool bf16, int G, size_t lds, int64_t B, hipStream_t s);
 
 }  // namespace recsa
