@@ -168,6 +168,7 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(DenseArgs a) {
   const int h = static_cast<int>(bh % a.Hkv);
 
   const int64_t qi = qb * QPB + wave * QPW + r32 / G;
+  const bool wave_active = qb * QPB + wave * QPW < a.n_q;   // uniform across the wave
   const int hh = r32 % G;
   const bool row_ok = qi < a.n_q;
   const int64_t pos = a.causal ? a.q_start + qi : a.n_tokens;
@@ -215,9 +216,10 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(DenseArgs a) {
     }
     __syncthreads();
 
-    // the tile's two 32-key halves one after the other, each a step of the online softmax
+    // the tile's two 32-key halves one after the other, each a step of the online softmax; a
+    // wave that owns no query (few queries, as in decoding) only helps stage the tiles
 #pragma unroll 1
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int kh = 0; kh < (wave_active ? 2 : 0); ++kh) {
       f32x16_t st;
 #pragma unroll
       for (int v = 0; v < 16; ++v) st[v] = 0.0f;
@@ -291,6 +293,177 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(DenseArgs a) {
         *reinterpret_cast<float4*>(dst + 32 * t + 8 * g4 + 4 * hl) =
             make_float4(o[t][4 * g4], o[t][4 * g4 + 1], o[t][4 * g4 + 2], o[t][4 * g4 + 3]);
     if (hl == 0) {
+      a.part_ml[2 * prow] = m_run;
+      a.part_ml[2 * prow + 1] = l_run;
+    }
+  }
+}
+
+// Few queries (decoding: every row of a KV head fits one 16-row wave): 16 (query, head) rows per
+// wave on v_mfma_f32_16x16x32_bf16, which wastes less of each tile than the 32-row kernel when
+// most rows are empty. Same data layout and results; the queries arrive rotated (use_rope = 0)
+// or are rotated here.
+template <int D, int G>
+__global__ __launch_bounds__(256) void dense_mfma16_kernel(DenseArgs a) {
+  constexpr int QPW = 16 / G, QPB = 4 * QPW;
+  constexpr int KT = 64;               // keys per tile
+  constexpr int KSTEPS = D / 32;       // MFMA k-steps over head_dim
+  constexpr int DT = D / 16;           // 16-dim output tiles
+  constexpr int HALF = D / 2;
+  constexpr int KPAD = D + 8;          // K tile row stride (bf16)
+  // V tile row stride (bf16): D/2 + 8 dwords, an odd multiple of 8, so the 8 rows that 32
+  // lanes of a transposing read touch fall in distinct bank groups
+  constexpr int VPAD = D + 16;
+  __shared__ __align__(16) uint16_t Ks[KT * KPAD];
+  __shared__ __align__(16) uint16_t Vs[KT * VPAD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int64_t qb = blockIdx.x, bh = blockIdx.y, split = blockIdx.z;
+  const int64_t b = bh / a.Hkv;
+  const int h = static_cast<int>(bh % a.Hkv);
+
+  const int64_t qi = qb * QPB + wave * QPW + r16 / G;
+  const int hh = r16 % G;
+  const bool row_ok = qi < a.n_q;
+  const int64_t pos = a.causal ? a.q_start + qi : a.n_tokens;
+  const int64_t row_kmax = a.causal ? pos + 1 : a.n_tokens;
+  const int64_t q_last = (qb * QPB + QPB < a.n_q ? qb * QPB + QPB : a.n_q) - 1;
+  const int64_t kmax_blk = a.causal ? a.q_start + q_last + 1 : a.n_tokens;
+  const int64_t k_lo = split * a.keys_per_split;
+  const int64_t k_hi = k_lo + a.keys_per_split < kmax_blk ? k_lo + a.keys_per_split : kmax_blk;
+
+  // rotated, bf16-rounded query fragments (B operand): dims 32m + 8*g4 + j
+  bf16x8_t qf[KSTEPS];
+  {
+    float x[KSTEPS][8];
+    const int64_t qoff = ((b * a.n_q + (row_ok ? qi : 0)) * a.Hq + static_cast<int64_t>(h) * G + hh) * D;
+#pragma unroll
+    for (int m = 0; m < KSTEPS; ++m) load8<true>(a.q, qoff + 32 * m + 8 * g4, x[m]);
+    if (a.use_rope) {
+#pragma unroll
+      for (int m = 0; m < KSTEPS / 2; ++m)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float c, s;
+          rope_cs(pos, a.iv.w[32 * m + 8 * g4 + j], c, s);
+          const float x1 = x[m][j], x2 = x[m + KSTEPS / 2][j];
+          const float p1 = x1 * c, p2 = x2 * s, p3 = x2 * c, p4 = x1 * s;
+          x[m][j] = p1 - p2;
+          x[m + KSTEPS / 2][j] = p3 + p4;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < KSTEPS; ++m)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[m][j] = static_cast<__bf16>(row_ok ? x[m][j] : 0.0f);
+  }
+
+  f32x4_t o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) o[t] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  for (int64_t k0 = k_lo; k0 < k_hi; k0 += KT) {
+    __syncthreads();
+    for (int c = tid; c < KT * (D / 8); c += 256) {
+      const int r = c / (D / 8), ch = c % (D / 8);
+      const int64_t key = k0 + r;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (key < k_hi) {
+        kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Kr) + (bh * a.kr_rows + key) * D + ch * 8);
+        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.V) + (bh * a.v_rows + key) * D + ch * 8);
+      }
+      *reinterpret_cast<uint4*>(&Ks[r * KPAD + ch * 8]) = kv;
+      *reinterpret_cast<uint4*>(&Vs[r * VPAD + ch * 8]) = vv;
+    }
+    __syncthreads();
+
+    // S^T: 4 sub-tiles of 16 keys x 16 rows; lane holds keys 16*s4 + 4*g4 + i of row r16
+    f32x4_t st[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      st[s4] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int m = 0; m < KSTEPS; ++m) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(&Ks[(16 * s4 + r16) * KPAD + 32 * m + 8 * g4]);
+        st[s4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qf[m], st[s4], 0, 0, 0);
+      }
+    }
+    float sv[4][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t key = k0 + 16 * s4 + 4 * g4 + i;
+        float v = st[s4][i] * a.scale;
+        if (!row_ok || key >= k_hi || key >= row_kmax) v = -INFINITY;
+        sv[s4][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = m_new == -INFINITY ? 1.0f : __expf(m_run - m_new);
+    float lsum = 0.0f;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = sv[s4][i] == -INFINITY ? 0.0f : __expf(sv[s4][i] - m_new);
+        sv[s4][i] = p;
+        lsum += p;
+      }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] *= alpha;
+
+    // O^T += V^T P^T over two 32-key blocks; the k-slot order (4*g4 + j, then 16 + 4*g4 + j)
+    // is the order the S^T lanes already hold
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8_t pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = static_cast<__bf16>(sv[2 * kb][i]);
+        pb[4 + i] = static_cast<__bf16>(sv[2 * kb + 1][i]);
+      }
+      // this lane addresses key 32kb + 4*g4 + r16/4 (and 16 keys on), dims 16t + 4*(r16%4) + 0..3;
+      // it receives dim 16t + r16 of keys 32kb + 4*g4 + 0..3 and 32kb + 16 + 4*g4 + 0..3
+      const uint16_t* vr = &Vs[(32 * kb + 4 * g4 + (r16 >> 2)) * VPAD + 4 * (r16 & 3)];
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const i16x4_t lo = lds_read_tr16(vr + 16 * t);
+        const i16x4_t hi = lds_read_tr16(vr + 16 * VPAD + 16 * t);
+        const i16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, o[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // o[t][i] = O^T[dim 16t + 4*g4 + i][row r16]
+  if (!row_ok) return;
+  if (a.n_splits == 1) {
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    float* dst = a.out + ((b * a.n_q + qi) * a.Hq + static_cast<int64_t>(h) * G + hh) * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+      *reinterpret_cast<float4*>(dst + 16 * t + 4 * g4) =
+          make_float4(o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
+    if (a.lse && g4 == 0)
+      a.lse[(b * a.n_q + qi) * a.Hq + static_cast<int64_t>(h) * G + hh] = l_run > 0.0f ? m_run + logf(l_run) : -INFINITY;
+  } else {
+    const int64_t rows = a.n_q * G;
+    const int64_t prow = (split * gridDim.y + bh) * rows + qi * G + hh;
+    float* dst = a.part_o + prow * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+      *reinterpret_cast<float4*>(dst + 16 * t + 4 * g4) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
+    if (g4 == 0) {
       a.part_ml[2 * prow] = m_run;
       a.part_ml[2 * prow + 1] = l_run;
     }
@@ -418,10 +591,15 @@ __global__ __launch_bounds__(64) void dense_valu_kernel(DenseArgs a) {
 
 template <int D, int G>
 static hipError_t launch_dense_bf16(const DenseArgs& a, int64_t B, hipStream_t s) {
-  constexpr int QPB = DenseGeom<G>::QPB;
-  const dim3 grid(static_cast<unsigned>((a.n_q + QPB - 1) / QPB), static_cast<unsigned>(B * a.Hkv),
-                  static_cast<unsigned>(a.n_splits));
-  hipLaunchKernelGGL((dense_mfma_kernel<D, G>), grid, dim3(256), 0, s, a);
+  if (a.n_q * G <= 16) {
+    const dim3 grid(1u, static_cast<unsigned>(B * a.Hkv), static_cast<unsigned>(a.n_splits));
+    hipLaunchKernelGGL((dense_mfma16_kernel<D, G>), grid, dim3(256), 0, s, a);
+  } else {
+    constexpr int QPB = DenseGeom<G>::QPB;
+    const dim3 grid(static_cast<unsigned>((a.n_q + QPB - 1) / QPB), static_cast<unsigned>(B * a.Hkv),
+                    static_cast<unsigned>(a.n_splits));
+    hipLaunchKernelGGL((dense_mfma_kernel<D, G>), grid, dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   const dim3 mg(static_cast<unsigned>(a.n_q * G), static_cast<unsigned>(B * a.Hkv));
