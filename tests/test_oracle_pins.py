@@ -568,3 +568,64 @@ def test_backward_without_pruning_is_dense_attention_gradient():
     np.testing.assert_allclose(g["dK"][0, 0], Kt.grad.numpy(), rtol=0, atol=1e-5)
     np.testing.assert_allclose(g["dV"][0, 0], Vt.grad.numpy(), rtol=0, atol=1e-5)
     assert np.all(g["dW"] == 0.0)
+
+
+# ------------------------------------------------------------------ pooler distillation
+
+def _distill_case(seed):
+    rng = np.random.default_rng(4000 + seed)
+    f, d, G, n, n_q = [3, 4][seed % 2], 8, 2, 150, 3
+    theta = [50.0, 0.0][seed % 2]
+    K = _rand(rng, (1, 1, n, d))
+    V = _rand(rng, (1, 1, n, d))
+    q = _rand(rng, (1, n_q, G, d))
+    W = (np.eye(d) + 0.3 / np.sqrt(d) * rng.standard_normal((d, d))).astype(np.float32)
+    target = rng.standard_normal((1, n_q, G, d)).astype(np.float32) * 0.3
+    k = [2] * 8
+    return f, d, G, n, n_q, theta, K, V, q, W, target, k
+
+
+def _fixed_sel_loss(Wx, K, V, q, target, f, n, k, theta, sels):
+    tot, N = 0.0, 0
+    for j in range(q.shape[1]):
+        r = brute_unit(q[0, j], K[0, 0], V[0, 0], Wx, n, f, k, theta, fixed_sel=sels[j])
+        diff = r["out"] - target[0, j].astype(np.float64)
+        tot += float(np.sum(diff * diff))
+        N += diff.size
+    return tot / N
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_distill_gradient_matches_finite_differences(seed):
+    """The pooler gradient of the distillation loss (mean squared output difference, selections
+    held fixed) equals central differences of that loss computed by the independent float64
+    brute force with the same kept sets."""
+    from oracle.distill import distill_step
+    f, d, G, n, n_q, theta, K, V, q, W, target, k = _distill_case(seed)
+    st = distill_step(K, V, W, q, target, f, k, "f32", lr=0.1, n_tokens=n, theta=theta)
+    sels = [st["results"][(0, j, 0)].sel for j in range(n_q)]
+    Wd = W.astype(np.float64)
+    assert abs(_fixed_sel_loss(Wd, K, V, q, target, f, n, k, theta, sels) - st["loss"]) <= 1e-6 * (1 + st["loss"])
+    rng = np.random.default_rng(seed)
+    eps = 1e-6
+    for _ in range(8):
+        i, j = (int(x) for x in rng.integers(0, d, 2))
+        Wp, Wm = Wd.copy(), Wd.copy()
+        Wp[i, j] += eps
+        Wm[i, j] -= eps
+        fd = (_fixed_sel_loss(Wp, K, V, q, target, f, n, k, theta, sels) -
+              _fixed_sel_loss(Wm, K, V, q, target, f, n, k, theta, sels)) / (2 * eps)
+        assert abs(fd - st["dW"][i, j]) <= 2e-6 + 1e-4 * abs(fd), (i, j, fd, st["dW"][i, j])
+
+
+def test_distill_step_lowers_the_loss():
+    """A small step against the gradient lowers the fixed-selection loss by about lr |dW|^2."""
+    from oracle.distill import distill_step
+    f, d, G, n, n_q, theta, K, V, q, W, target, k = _distill_case(0)
+    lr = 0.05
+    st = distill_step(K, V, W, q, target, f, k, "f32", lr=lr, n_tokens=n, theta=theta)
+    sels = [st["results"][(0, j, 0)].sel for j in range(n_q)]
+    before = _fixed_sel_loss(W.astype(np.float64), K, V, q, target, f, n, k, theta, sels)
+    after = _fixed_sel_loss(st["W_master"], K, V, q, target, f, n, k, theta, sels)
+    drop = lr * float(np.sum(st["dW"] ** 2))
+    assert drop > 0 and before - after == pytest.approx(drop, rel=0.2)
