@@ -199,7 +199,8 @@ int32_t recsa_decode_step(const recsa_shape_t* shape, const void* q, const void*
  *   dout [dev]: float32 [B][n_q][H_q][d]; dlse [dev]: float32 [B][n_q][H_q] (nullable: zero).
  *   dq [dev]: float32 [B][n_q][H_q][d], written.
  *   dK, dV [dev]: float32 [B][H_kv][capacity][d], and dW [dev]: float32 [d][d], added to (zero
- *   them before the first call; calls over successive chunks of queries accumulate).
+ *   them before the first call; calls over successive chunks of queries accumulate). dK and dV
+ *   may both be NULL: the token rows' gradients are then not computed (dq and dW are).
  *   workspace: recsa_backward_workspace_bytes(shape, n_max, k, n_levels) with n_max = n_tokens
  *   (decode) or q_start + n_q: the RoPE table and float32 node gradients.
  * Row gradients are summed with float32 atomic adds, in an order the hardware chooses, so they
@@ -214,6 +215,28 @@ int32_t recsa_backward(const recsa_shape_t* shape, int32_t causal, const void* q
                        const float* dout, const float* dlse,
                        float* dq, float* dK, float* dV, float* dW,
                        void* workspace, int64_t ws_bytes, void* stream);
+
+/* One step of pooler distillation on a fixed batch of decode queries [Abstract; Core Idea: the
+ * pooler is learned by distilling from full attention]. The pages give neither loss nor
+ * optimiser. Reading: loss = mean over (sequence, query, query head, dimension) of
+ * (out - target)^2, out being recsa_decode's output and target full attention's (e.g.
+ * recsa_dense_ref_attn on the same queries); the gradient is taken with the selections held
+ * fixed (recsa_backward), and W is updated by plain gradient descent on a float32 master copy.
+ * In order on `stream`: the tree is rebuilt with the current W (all nodes complete at
+ * n_tokens), the queries are decoded (selections recorded), dL/dout = 2 (out - target) / N and
+ * the loss are formed, dW is computed, then W_master -= lr * dW and W = round(W_master).
+ *   q [dev]: [B][n_q][H_q][d]; K, V [dev]: caches; target [dev]: float32 [B][n_q][H_q][d].
+ *   W_master [dev]: float32 [d][d], updated; W [dev]: [d][d] storage type, the pooler this step
+ *   uses, overwritten with the rounded update; tree [dev]: rebuilt (recsa_tree_bytes).
+ *   loss [dev]: one float32, the loss at the W this step used.
+ *   workspace: recsa_distill_workspace_bytes(shape, n_tokens, n_q, k, n_levels).
+ * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED, WORKSPACE. */
+int64_t recsa_distill_workspace_bytes(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q,
+                                      const int32_t* k_per_level, int32_t n_levels);
+int32_t recsa_distill_step(const recsa_shape_t* shape, const void* q, int64_t n_q, const void* K,
+                           const void* V, int64_t n_tokens, const int32_t* k_per_level, int32_t n_levels,
+                           const float* target, float lr, float* W_master, void* W, void* tree,
+                           float* loss, void* workspace, int64_t ws_bytes, void* stream);
 
 /* Dense softmax attention with standard RoPE at the original positions -- the comparator the
  * method is timed against [Abstract]; also RecSA's limit when every level keeps everything.

@@ -501,9 +501,9 @@ int32_t recsa_backward(const recsa_shape_t* shape, int32_t causal, const void* q
   if (rc) return rc;
   if (n_q == 0) return RECSA_OK;
   const int T = levels_of(n_max, I.f);
-  if (!q || !out || !lse || !sel || !dout || !dq || !dK || !dV || !dW || (n_max > 0 && (!K || !V)) ||
-      (T > 0 && (!tree || !W)))
-    return fail(RECSA_ERR_INVALID_ARG, "q, K, V, W, tree, out, lse, sel, dout, dq, dK, dV or dW is NULL");
+  if (!q || !out || !lse || !sel || !dout || !dq || !dW || (n_max > 0 && (!K || !V)) || (T > 0 && (!tree || !W)))
+    return fail(RECSA_ERR_INVALID_ARG, "q, K, V, W, tree, out, lse, sel, dout, dq or dW is NULL");
+  if ((dK == nullptr) != (dV == nullptr)) return fail(RECSA_ERR_INVALID_ARG, "dK and dV must both be given or both be NULL");
   if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(tree) || !aligned16(out) ||
       !aligned16(dout) || !aligned16(dq) || !aligned16(dK) || !aligned16(dV) || !aligned16(dW) || !aligned16(workspace))
     return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
@@ -578,6 +578,95 @@ int32_t recsa_backward(const recsa_shape_t* shape, int32_t causal, const void* q
     e = recsa::launch_tree_push(p, static_cast<int>(I.d), I.bf16, st);
     if (e != hipSuccess) return hip_fail(e, "tree gradient launch");
   }
+  return RECSA_OK;
+}
+
+// Pooler distillation step: workspace sub-buffers, each 256-byte aligned.
+struct DistillPlan {
+  int64_t dec_ws, out, lse, sel, dout, dq, dW, partial, bwd_ws, total;
+  int32_t width;
+};
+
+static int64_t al256(int64_t x) { return (x + 255) / 256 * 256; }
+
+static int32_t distill_plan(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q, const int32_t* k,
+                            int32_t n_levels, DistillPlan* p) {
+  Info I;
+  int32_t rc = check_shape(shape, &I);
+  if (rc) return rc;
+  if (n_q < 1) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 1");
+  if (n_tokens < 0) return fail(RECSA_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (n_tokens > I.cap)
+    return fail(RECSA_ERR_CAPACITY, "n_tokens %lld exceeds the capacity %lld", (long long)n_tokens, (long long)I.cap);
+  rc = check_k(k, n_levels, levels_of(n_tokens, I.f));
+  if (rc) return rc;
+  const int64_t dec = recsa_workspace_bytes(shape, n_tokens, k, n_levels);
+  const int64_t bwd = recsa_backward_workspace_bytes(shape, n_tokens, k, n_levels);
+  if (dec < 0 || bwd < 0) return RECSA_ERR_UNSUPPORTED;
+  p->width = std::max<int32_t>(max_kept(n_tokens, I.f, k), 1);
+  const int64_t rows = I.B * n_q * I.Hq;
+  int64_t o = 0;
+  p->dec_ws = o; o += al256(dec);
+  p->out = o; o += al256(rows * I.d * 4);
+  p->lse = o; o += al256(rows * 4);
+  p->sel = o; o += al256(I.B * n_q * I.Hkv * std::max(n_levels, 1) * static_cast<int64_t>(p->width) * 4);
+  p->dout = o; o += al256(rows * I.d * 4);
+  p->dq = o; o += al256(rows * I.d * 4);
+  p->dW = o; o += al256(I.d * I.d * 4);
+  p->partial = o; o += al256(static_cast<int64_t>(recsa::distill_loss_blocks(rows * I.d)) * 4);
+  p->bwd_ws = o; o += al256(bwd);
+  p->total = o;
+  return RECSA_OK;
+}
+
+int64_t recsa_distill_workspace_bytes(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q, const int32_t* k,
+                                      int32_t n_levels) {
+  DistillPlan p;
+  if (distill_plan(shape, n_tokens, n_q, k, n_levels, &p)) return -1;
+  return p.total;
+}
+
+int32_t recsa_distill_step(const recsa_shape_t* shape, const void* q, int64_t n_q, const void* K, const void* V,
+                           int64_t n_tokens, const int32_t* k, int32_t n_levels, const float* target, float lr,
+                           float* W_master, void* W, void* tree, float* loss, void* workspace, int64_t ws_bytes,
+                           void* stream) {
+  DistillPlan p;
+  int32_t rc = distill_plan(shape, n_tokens, n_q, k, n_levels, &p);
+  if (rc) return rc;
+  Info I;
+  check_shape(shape, &I);
+  if (!std::isfinite(lr)) return fail(RECSA_ERR_INVALID_ARG, "lr must be finite");
+  if (!q || !target || !W_master || !W || !loss || !workspace || (n_tokens > 0 && (!K || !V)) ||
+      (levels_of(I.cap, I.f) > 0 && !tree))
+    return fail(RECSA_ERR_INVALID_ARG, "q, K, V, target, W_master, W, tree, loss or workspace is NULL");
+  if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(target) || !aligned16(W_master) || !aligned16(W) ||
+      !aligned16(tree) || !aligned16(workspace))
+    return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (ws_bytes < p.total)
+    return fail(RECSA_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes, (long long)p.total);
+  char* ws = static_cast<char*>(workspace);
+  float* out = reinterpret_cast<float*>(ws + p.out);
+  float* lse = reinterpret_cast<float*>(ws + p.lse);
+  int32_t* sel = reinterpret_cast<int32_t*>(ws + p.sel);
+  float* dout = reinterpret_cast<float*>(ws + p.dout);
+  float* dq = reinterpret_cast<float*>(ws + p.dq);
+  float* dW = reinterpret_cast<float*>(ws + p.dW);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = recsa_build_tree(shape, K, V, W, 0, n_tokens, tree, stream);
+  if (rc) return rc;
+  rc = recsa_decode(shape, q, n_q, K, V, tree, n_tokens, k, n_levels, out, lse, sel, p.width, ws + p.dec_ws,
+                    p.out - p.dec_ws, stream);
+  if (rc) return rc;
+  const int64_t n = I.B * n_q * I.Hq * I.d;
+  hipError_t e = recsa::launch_distill_loss(out, target, dout, reinterpret_cast<float*>(ws + p.partial), loss, n, st);
+  if (e != hipSuccess) return hip_fail(e, "distillation loss launch");
+  e = recsa::launch_fill_zero(dW, I.d * I.d, st);
+  if (e != hipSuccess) return hip_fail(e, "gradient clear");
+  rc = recsa_backward(shape, 0, q, 0, n_q, n_tokens, K, V, W, tree, k, n_levels, out, lse, sel, p.width, dout, nullptr,
+                      dq, nullptr, nullptr, dW, ws + p.bwd_ws, p.total - p.bwd_ws, stream);
+  if (rc) return rc;
+  e = recsa::launch_distill_update(W_master, dW, W, lr, I.d * I.d, I.bf16, st);
+  if (e != hipSuccess) return hip_fail(e, "pooler update launch");
   return RECSA_OK;
 }
 

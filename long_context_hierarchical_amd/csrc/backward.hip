@@ -219,7 +219,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ba
         rst[srg][1][HALF + 4 * ssub + e] = du[4 + e];
       }
       if (ssub == 0) {
-        roff[srg] = valid ? (rowbase + g) * D : -1;
+        roff[srg] = valid && gk != nullptr ? (rowbase + g) * D : -1;   // no row gradients wanted: skip
       }
       wave_sync();
 #pragma unroll
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void tree_push_kernel(TreePushArgs a) {
       for (int u = 0; u < NPG; ++u) dmg[nd0 + u][i] = dm[u] / ff;
     }
     __syncthreads();
-    for (int idx = tid; idx < NB * Q4; idx += NT) {
+    for (int idx = tid; idx < NB * Q4 && a.ck != nullptr; idx += NT) {
       const int nd = idx / Q4, q = idx % Q4;
       if (!touched[nd]) continue;
       const float4 dk = reinterpret_cast<const float4*>(dmg[nd])[q];

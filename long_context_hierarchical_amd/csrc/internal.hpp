@@ -155,6 +155,14 @@ struct TreePushArgs {
 hipError_t launch_tree_push(const TreePushArgs& a, int d, bool bf16, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
+// ---------------------------------------------------------------- pooler distillation
+int distill_loss_blocks(int64_t n);
+// dout = 2 (out - target) / n and loss = mean of (out - target)^2 (partial: distill_loss_blocks(n) floats)
+hipError_t launch_distill_loss(const float* out, const float* target, float* dout, float* partial, float* loss,
+                               int64_t n, hipStream_t s);
+// W_master -= lr * dW; W = W_master rounded to the storage type (n = d * d)
+hipError_t launch_distill_update(float* Wm, const float* dW, void* W, float lr, int64_t n, bool bf16, hipStream_t s);
+
 // ---------------------------------------------------------------- dense reference attention
 // Keys rotated at their own positions: Kr[bh][p] = round(rot(K[bh][p], p)), p < n
 // (K rows per slice: cap; Kr rows per slice: kr_rows).

@@ -21,7 +21,8 @@ INT32_MAX = 2 ** 31 - 1
 EXPORTS = (
     "recsa_abi_version", "recsa_last_error", "recsa_num_levels", "recsa_tree_bytes", "recsa_level_offset",
     "recsa_sel_width", "recsa_workspace_bytes", "recsa_build_tree", "recsa_decode", "recsa_prefill",
-    "recsa_decode_step", "recsa_backward_workspace_bytes", "recsa_backward",
+    "recsa_decode_step", "recsa_backward_workspace_bytes", "recsa_backward", "recsa_distill_workspace_bytes",
+    "recsa_distill_step",
     "recsa_dense_workspace_bytes", "recsa_dense_ref_attn", "recsa_rotate_keys",
 )
 RECSA_DENSE_CAUSAL, RECSA_DENSE_KEYS_ROTATED = 1, 2
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
             "recsa_prefill": (I32, [SP, P, I64, I64, P, P, P, K, I32, P, P, P, I32, P, I64, P]),
             "recsa_decode_step": (I32, [SP, P, P, P, P, P, P, P, I64, K, I32, P, P, P, I32, P, I64, P]),
             "recsa_backward_workspace_bytes": (I64, [SP, I64, K, I32]),
+            "recsa_distill_workspace_bytes": (I64, [SP, I64, I64, K, I32]),
+            "recsa_distill_step": (I32, [SP, P, I64, P, P, I64, K, I32, P, ctypes.c_float, P, P, P, P, P, I64, P]),
             "recsa_backward": (I32, [SP, I32, P, I64, I64, I64, P, P, P, P, K, I32, P, P, P, I32, P, P, P, P, P, P,
                                      P, I64, P]),
             "recsa_dense_workspace_bytes": (I64, [SP, I64, I64, I32]),
@@ -207,6 +210,21 @@ def recsa_backward(shape: Shape, causal: bool, q, q_start: int, n_tokens: int, K
                                 _p(V), _p(W), _p(tree), k, nl, _p(out), _p(lse), _p(sel), sel_width, _p(dout),
                                 _p(dlse), _p(dq), _p(dK), _p(dV), _p(dW), _p(workspace), ws_bytes,
                                 _stream(stream)))
+
+
+def recsa_distill_workspace_bytes(shape: Shape, n_tokens: int, n_q: int, k_levels) -> int:
+    k, nl = _k(k_levels)
+    return _nbytes(lib().recsa_distill_workspace_bytes(ctypes.byref(shape.c()), n_tokens, n_q, k, nl))
+
+
+def recsa_distill_step(shape: Shape, q, K, V, n_tokens: int, k_levels, target, lr: float, W_master, W, tree, loss,
+                       workspace, stream=None):
+    k, nl = _k(k_levels)
+    n_q = q.shape[1]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().recsa_distill_step(ctypes.byref(shape.c()), _p(q), n_q, _p(K), _p(V), n_tokens, k, nl, _p(target),
+                                    float(lr), _p(W_master), _p(W), _p(tree), _p(loss), _p(workspace), ws_bytes,
+                                    _stream(stream)))
 
 
 def recsa_dense_ref_attn(shape: Shape, q, q_start: int, K, V, n_tokens: int, mode: int, out, lse=None,
