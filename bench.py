@@ -669,8 +669,36 @@ def main():
                                             dK, dV, dW, workspace=bws), 2)
         bwd["prefill_last_chunk"] = {"ms_per_call": round(ms, 4), "tokens_per_call": w.B * c,
                                      "tokens_per_s": round(w.B * c / (ms * 1e-3), 1), "forward_ms": round(fwd_ms, 4)}
-        res["breakdown"]["backward"] = bwd
         del bws, dK, dV, dW, dout, dq, qc, cout, clse, csel, cdout, cdq
+        # pooler distillation: one step = tree rebuild with the current pooler, decode of the 1024
+        # queries, squared-error loss against full attention's outputs (computed once, outside
+        # the timed steps), gradient for W only, update
+        mode = R.RECSA_DENSE_KEYS_ROTATED
+        Kr = torch.empty_like(K)
+        R.recsa_rotate_keys(sh, K, w.L, Kr)
+        tgt = torch.empty_like(out)
+        dws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, w.n_queries, mode), 16), dtype=torch.uint8,
+                          device=dev)
+        R.recsa_dense_ref_attn(sh, q, 0, Kr, V, w.L, mode, tgt, None, dws)
+        del Kr, dws
+        Wm = W.float().clone()
+        Wd = W.clone()
+        dtree = torch.zeros_like(tree)
+        dloss = torch.zeros(4, dtype=torch.float32, device=dev)
+        dws = torch.zeros(R.recsa_distill_workspace_bytes(sh, w.L, w.n_queries, k), dtype=torch.uint8, device=dev)
+        losses = []
+
+        def dstep():
+            R.recsa_distill_step(sh, q, K, V, w.L, k, tgt, 1.0, Wm, Wd, dtree, dloss, dws)
+
+        dstep()
+        losses.append(float(dloss[0].cpu()))
+        ms = timed(dstep, 3)
+        losses.append(float(dloss[0].cpu()))
+        bwd["distill_step"] = {"ms_per_step": round(ms, 4), "queries_per_step": n_queries,
+                               "loss_first_last": [round(losses[0], 8), round(losses[-1], 8)]}
+        res["breakdown"]["backward"] = bwd
+        del Wm, Wd, dtree, dloss, dws, tgt
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
