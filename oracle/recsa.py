@@ -377,43 +377,58 @@ class TreeCache:
         return ent[0], ent[1], ent[2]
 
 
-def _all_units(B, n_q, Hkv):
-    return [(b, j, h) for b in range(B) for j in range(n_q) for h in range(Hkv)]
+def _all_units(B, n_q, groups):
+    return [(b, j, h) for b in range(B) for j in range(n_q) for h in range(groups)]
+
+
+def _groups(Hq: int, Hkv: int, select_heads):
+    """(query heads per selection group, groups per sequence). By default the G = Hq / Hkv heads
+    of a KV head select together [Abstract: per-query selection over the heads that share the
+    KV cache]; a divisor Gs of G splits them into groups that select independently over the
+    same tree and cache (Gs = 1: every head selects alone)."""
+    G = Hq // Hkv
+    Gs = G if not select_heads else int(select_heads)
+    if G % Gs:
+        raise ValueError("select_heads must divide the query heads of a KV head")
+    return Gs, Hq // Gs
 
 
 def decode(K, V, W, q, n_tokens: int, f: int, k_levels, dtype: str, theta: float = 1.0e6,
-           scale=None, units=None, cache: TreeCache | None = None) -> dict:
+           scale=None, units=None, cache: TreeCache | None = None, select_heads=None) -> dict:
     """Decode: every query of q [B][n_q][Hq][d] at position n_tokens against the first
-    n_tokens cached tokens of K, V [B][Hkv][cap][d] (storage form). Returns {(b, j, h): UnitResult}.
+    n_tokens cached tokens of K, V [B][Hkv][cap][d] (storage form). Returns {(b, j, g): UnitResult}
+    with g the selection group (the KV head by default; group g reads KV head g // (G / Gs)).
     """
     B, n_q, Hq, d = q.shape
     Hkv = K.shape[1]
     G = Hq // Hkv
+    Gs, groups = _groups(Hq, Hkv, select_heads)
     cache = cache or TreeCache(K, V, W, f, dtype)
     out = {}
-    for (b, j, h) in (units if units is not None else _all_units(B, n_q, Hkv)):
-        Kf, Vf, tree = cache.get(b, h, n_tokens)
-        qg = from_storage(q[b, j, h * G:(h + 1) * G], dtype)
-        out[(b, j, h)] = attend_unit(qg, Kf, Vf, tree, n_tokens, f, k_levels, dtype, theta, scale)
+    for (b, j, g) in (units if units is not None else _all_units(B, n_q, groups)):
+        Kf, Vf, tree = cache.get(b, g // (G // Gs), n_tokens)
+        qg = from_storage(q[b, j, g * Gs:(g + 1) * Gs], dtype)
+        out[(b, j, g)] = attend_unit(qg, Kf, Vf, tree, n_tokens, f, k_levels, dtype, theta, scale)
     return out
 
 
 def prefill(K, V, W, q, q_start: int, f: int, k_levels, dtype: str, theta: float = 1.0e6,
-            scale=None, units=None, cache: TreeCache | None = None) -> dict:
+            scale=None, units=None, cache: TreeCache | None = None, select_heads=None) -> dict:
     """Causal prefill: query j of q [B][n_q][Hq][d] sits at position t = q_start + j and sees
     tokens 0..t including itself, i.e. a descent over the prefix n = t + 1 with only the
-    nodes complete at n visible. Returns {(b, j, h): UnitResult}.
+    nodes complete at n visible. Returns {(b, j, g): UnitResult} (groups as in decode).
     """
     B, n_q, Hq, d = q.shape
     Hkv = K.shape[1]
     G = Hq // Hkv
+    Gs, groups = _groups(Hq, Hkv, select_heads)
     cache = cache or TreeCache(K, V, W, f, dtype)
     out = {}
-    for (b, j, h) in (units if units is not None else _all_units(B, n_q, Hkv)):
+    for (b, j, g) in (units if units is not None else _all_units(B, n_q, groups)):
         t = q_start + j
-        Kf, Vf, tree = cache.get(b, h, q_start + n_q)
-        qg = from_storage(q[b, j, h * G:(h + 1) * G], dtype)
-        out[(b, j, h)] = attend_unit(qg, Kf, Vf, tree, t + 1, f, k_levels, dtype, theta, scale,
+        Kf, Vf, tree = cache.get(b, g // (G // Gs), q_start + n_q)
+        qg = from_storage(q[b, j, g * Gs:(g + 1) * Gs], dtype)
+        out[(b, j, g)] = attend_unit(qg, Kf, Vf, tree, t + 1, f, k_levels, dtype, theta, scale,
                                      self_in=True)
     return out
 

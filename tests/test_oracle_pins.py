@@ -629,3 +629,47 @@ def test_distill_step_lowers_the_loss():
     after = _fixed_sel_loss(st["W_master"], K, V, q, target, f, n, k, theta, sels)
     drop = lr * float(np.sum(st["dW"] ** 2))
     assert drop > 0 and before - after == pytest.approx(drop, rel=0.2)
+
+
+# ------------------------------------------------------------------ heads selecting alone
+
+def test_heads_selecting_alone_match_brute_force_per_head():
+    """select_heads = 1: each query head descends on its own logit over its KV head's tree,
+    as the float64 brute force with that single head does."""
+    from oracle import decode
+    rng = np.random.default_rng(21)
+    f, d, n, Hkv, G = 4, 16, 300, 2, 2
+    K, V = _rand(rng, (1, Hkv, n, d)), _rand(rng, (1, Hkv, n, d))
+    q = _rand(rng, (1, 2, Hkv * G, d))
+    W = (np.eye(d) + 0.3 / np.sqrt(d) * rng.standard_normal((d, d))).astype(np.float32)
+    k = [2] * 6
+    res = decode(K, V, W, q, n, f, k, "f32", 50.0, select_heads=1)
+    assert len(res) == 2 * Hkv * G
+    for (b, j, g), r in res.items():
+        bu = brute_unit(q[b, j, g:g + 1], K[b, g // G], V[b, g // G], W, n, f, k, 50.0)
+        if any(r.flags.values()) or any(x < 1e-5 for x in bu["gap"].values()):
+            continue
+        assert r.sel == bu["sel"]
+        np.testing.assert_allclose(r.out, bu["out"], rtol=0, atol=1e-6)
+
+
+def test_identical_heads_select_alone_as_together():
+    """Heads that are copies of one another score candidates alike, so selecting alone or as a
+    group keeps the same nodes (the group score is G times each head's logit) and gives the
+    same outputs; select_heads = G is the default grouping."""
+    from oracle import decode
+    rng = np.random.default_rng(22)
+    f, d, n, G = 4, 16, 260, 4
+    K, V = _rand(rng, (1, 1, n, d)), _rand(rng, (1, 1, n, d))
+    q1 = _rand(rng, (1, 3, 1, d))
+    q = np.repeat(q1, G, axis=2)
+    W = (np.eye(d) + 0.3 / np.sqrt(d) * rng.standard_normal((d, d))).astype(np.float32)
+    k = [2] * 6
+    grp = decode(K, V, W, q, n, f, k, "f32", 50.0)
+    alone = decode(K, V, W, q, n, f, k, "f32", 50.0, select_heads=1)
+    same = decode(K, V, W, q, n, f, k, "f32", 50.0, select_heads=G)
+    for j in range(3):
+        for g in range(G):
+            assert alone[(0, j, g)].sel == grp[(0, j, 0)].sel
+            np.testing.assert_allclose(alone[(0, j, g)].out[0], grp[(0, j, 0)].out[g], rtol=0, atol=1e-9)
+        np.testing.assert_array_equal(same[(0, j, 0)].out, grp[(0, j, 0)].out)
