@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define RECSA_ABI_VERSION 1
+#define RECSA_ABI_VERSION 2
 #define RECSA_MAX_LEVELS 32
 
 typedef enum {
@@ -77,6 +77,11 @@ typedef struct {
   int64_t capacity;       /* tokens per (sequence, KV head) slice of K and V; sizes the tree */
   float softmax_scale;    /* 0 => 1/sqrt(d), rounded to float32 */
   float rope_theta;       /* RoPE base (1e6 for Qwen3-style models); 0 disables the rotation */
+  int32_t select_heads;   /* query heads that select together: 0 (or G) = the G heads of a KV head
+                             share one selection (their logits summed); a divisor of G makes smaller
+                             groups select independently over the same tree and cache (1 = every
+                             head alone). recsa_decode and recsa_prefill support every divisor;
+                             the other entry points need 0 or G. */
 } recsa_shape_t;
 
 /* ABI version (RECSA_ABI_VERSION). */
@@ -128,8 +133,9 @@ int32_t recsa_build_tree(const recsa_shape_t* shape, const void* K, const void* 
  *   k_l >= 0, INT32_MAX = keep everything).
  *   out [dev]: float32 [B][n_q][H_q][d]; lse [dev] (nullable): float32 [B][n_q][H_q], log of the
  *   softmax denominator (-inf and out = 0 when there is no entry, i.e. n_tokens = 0).
- *   sel [dev] (nullable): int32 [B][n_q][H_kv][n_levels][sel_width], the kept node ids of level
- *   l in row l-1, ascending, padded with -1; sel_width >= recsa_sel_width(n_tokens, n_tokens).
+ *   sel [dev] (nullable): int32 [B][n_q][groups][n_levels][sel_width], the kept node ids of level
+ *   l in row l-1, ascending, padded with -1; sel_width >= recsa_sel_width(n_tokens, n_tokens);
+ *   groups = H_q / select_heads (H_kv by default).
  *   workspace [dev]: ws_bytes >= recsa_workspace_bytes(shape, n_tokens, k, n_levels).
  * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED (candidate lists too long for on-chip memory),
  * WORKSPACE. */

@@ -40,6 +40,7 @@ constexpr int64_t kTableAlign = 256;
 
 struct Info {
   int64_t B, Hkv, Hq, d, f, G, cap;
+  int64_t Gs;     // query heads per selection group (G by default)
   bool bf16;
   int64_t esz;
   float scale, theta;
@@ -76,6 +77,16 @@ int32_t check_shape(const recsa_shape_t* s, Info* o) {
   o->esz = o->bf16 ? 2 : 4;
   o->scale = s->softmax_scale > 0.0f ? s->softmax_scale : static_cast<float>(1.0 / std::sqrt(static_cast<double>(s->head_dim)));
   o->theta = s->rope_theta;
+  if (s->select_heads < 0 || (s->select_heads > 0 && G % s->select_heads != 0))
+    return fail(RECSA_ERR_INVALID_ARG, "select_heads (%d) must be 0 or divide the %d query heads of a KV head",
+                s->select_heads, G);
+  o->Gs = s->select_heads > 0 ? s->select_heads : G;
+  return RECSA_OK;
+}
+
+// entry points whose kernels select per whole KV head group only
+int32_t need_group_selection(const Info& I) {
+  if (I.Gs != I.G) return fail(RECSA_ERR_UNSUPPORTED, "this entry point needs select_heads = 0 (or %lld)", (long long)I.G);
   return RECSA_OK;
 }
 
@@ -178,7 +189,7 @@ int32_t prepare_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, c
   int32_t rc = check_shape(shape, &I);
   if (rc) return rc;
   if (n_q < 0) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 0");
-  if (n_q * I.Hkv > INT32_MAX || I.B > 65535) return fail(RECSA_ERR_UNSUPPORTED, "grid too large");
+  if (n_q * I.Hq > INT32_MAX || I.B > 65535) return fail(RECSA_ERR_UNSUPPORTED, "grid too large");
   const int64_t n_max = prefill ? q_start + n_q : n_fixed;
   const int64_t n_min = prefill ? q_start + 1 : n_fixed;
   if (prefill && q_start < 0) return fail(RECSA_ERR_INVALID_ARG, "q_start must be >= 0");
@@ -208,7 +219,7 @@ int32_t prepare_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, c
   // chunks of zcap candidates, so an unbounded token list (no pruning) takes chunks of 256
   const int64_t zneed = std::max<int64_t>(bd.csel, std::min<int64_t>(bd.c0, 256));
   const int zcap = static_cast<int>((zneed + 15) / 16 * 16);
-  const size_t lds = recsa::attend_lds_bytes(static_cast<int>(I.d), static_cast<int>(I.G), static_cast<int>(bd.smax),
+  const size_t lds = recsa::attend_lds_bytes(static_cast<int>(I.d), static_cast<int>(I.Gs), static_cast<int>(bd.smax),
                                              zcap);
   if (lds > kMaxLds) return fail(RECSA_ERR_UNSUPPORTED, "needs %zu bytes of LDS (max %zu)", lds, kMaxLds);
   const int64_t need_ws = table_bytes(I, bd.P);
@@ -230,7 +241,9 @@ int32_t prepare_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, c
   a.n_fixed = n_fixed;
   a.q_start = q_start;
   a.prefill = prefill ? 1 : 0;
-  a.Hkv = static_cast<int32_t>(I.Hkv);
+  a.Hkv = static_cast<int32_t>(I.Hq / I.Gs);
+  a.Hkv_kv = static_cast<int32_t>(I.Hkv);
+  a.kv_div = static_cast<int32_t>(I.G / I.Gs);
   a.Hq = static_cast<int32_t>(I.Hq);
   a.f = static_cast<int32_t>(I.f);
   a.n_levels = n_levels;
@@ -250,7 +263,7 @@ int32_t prepare_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, c
 }
 
 int32_t launch_planned_attend(const AttendPlan& pl, hipStream_t st) {
-  hipError_t e = recsa::launch_attend(pl.a, static_cast<int>(pl.I.d), pl.I.bf16, static_cast<int>(pl.I.G), pl.lds,
+  hipError_t e = recsa::launch_attend(pl.a, static_cast<int>(pl.I.d), pl.I.bf16, static_cast<int>(pl.I.Gs), pl.lds,
                                       pl.I.B, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return RECSA_OK;
@@ -487,6 +500,8 @@ int32_t recsa_backward(const recsa_shape_t* shape, int32_t causal, const void* q
   Info I;
   int32_t rc = check_shape(shape, &I);
   if (rc) return rc;
+  rc = need_group_selection(I);
+  if (rc) return rc;
   if (causal != 0 && causal != 1) return fail(RECSA_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (n_q < 0) return fail(RECSA_ERR_INVALID_ARG, "n_q must be >= 0");
   if (n_q * I.Hkv > INT32_MAX || I.B > 65535) return fail(RECSA_ERR_UNSUPPORTED, "grid too large");
@@ -635,6 +650,8 @@ int32_t recsa_distill_step(const recsa_shape_t* shape, const void* q, int64_t n_
   if (rc) return rc;
   Info I;
   check_shape(shape, &I);
+  rc = need_group_selection(I);
+  if (rc) return rc;
   if (!std::isfinite(lr)) return fail(RECSA_ERR_INVALID_ARG, "lr must be finite");
   if (!q || !target || !W_master || !W || !loss || !workspace || (n_tokens > 0 && (!K || !V)) ||
       (levels_of(I.cap, I.f) > 0 && !tree))

@@ -329,7 +329,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
   const int h = static_cast<int>(unit % a.Hkv);
   const int64_t n = a.prefill ? a.q_start + j + 1 : a.n_fixed;
   const int f = a.f;
-  const int64_t bh = b * a.Hkv + h;
+  const int64_t bh = b * a.Hkv_kv + h / a.kv_div;   // the selection group's KV head
 
   // raw query heads of the KV group -> LDS (float)
   {

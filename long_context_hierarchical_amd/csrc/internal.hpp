@@ -89,7 +89,9 @@ struct AttnArgs {
   int64_t n_fixed;      // decode: visible tokens
   int64_t q_start;      // prefill: position of query 0
   int32_t prefill;      // 1: query j sees n = q_start + j + 1 tokens, own token included
-  int32_t Hkv, Hq, f;
+  int32_t Hkv, Hq, f;   // Hkv: selection groups per sequence (= KV heads unless heads select alone)
+  int32_t Hkv_kv;       // KV heads per sequence
+  int32_t kv_div;       // selection groups per KV head (group h reads KV head h / kv_div)
   int32_t n_levels, sel_width;
   float scale;
   int32_t use_rope;

@@ -39,6 +39,7 @@ class _Shape(ctypes.Structure):
         ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("fanout", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("capacity", ctypes.c_int64), ("softmax_scale", ctypes.c_float), ("rope_theta", ctypes.c_float),
+        ("select_heads", ctypes.c_int32),
     ]
 
 
@@ -53,11 +54,12 @@ class Shape:
     capacity: int
     softmax_scale: float = 0.0
     rope_theta: float = 1.0e6
+    select_heads: int = 0     # query heads per selection (0 = the KV head's group)
 
     def c(self) -> _Shape:
         return _Shape(self.batch, self.n_kv_heads, self.n_q_heads, self.head_dim, self.fanout,
                       RECSA_BF16 if self.dtype == "bf16" else RECSA_F32, self.capacity,
-                      self.softmax_scale, self.rope_theta)
+                      self.softmax_scale, self.rope_theta, self.select_heads)
 
     @property
     def torch_dtype(self):

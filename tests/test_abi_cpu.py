@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(R.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert R.recsa_abi_version() == 1
+    assert R.recsa_abi_version() == 2
 
 
 def _shape(**kw):
@@ -148,3 +148,8 @@ def test_error_paths_return_status_before_launch():
                    stream=ns) == -1
     assert _status(bwd, sh, False, q, 0, 4096, *args, workspace=small_ws, stream=ns) == -5
     assert R.recsa_backward_workspace_bytes(sh, 4096, k) > R.recsa_workspace_bytes(sh, 4096, k)
+    # heads selecting in groups smaller than their KV head: a divisor of G; gradients need whole groups
+    alone = _shape(capacity=4096, select_heads=1)
+    assert _status(bwd, alone, False, q, 0, 4096, *args, workspace=t, stream=ns) == -3
+    assert _status(R.recsa_decode, _shape(capacity=4096, select_heads=3), q, t, t, t, 4096, k, t, None, None, 0, t,
+                   ns) == -1

@@ -8,7 +8,9 @@ import pytest
 import torch
 
 import oracle
+import gpu_util
 from gpu_util import TOL, Gpu, compare_unit, storage_bits
+from long_context_hierarchical_amd import recsa as R
 from synthetic import WORKLOADS, Workload, gen_decode_inputs, with_overrides
 
 pytestmark = pytest.mark.gpu
@@ -277,3 +279,45 @@ def test_prefill_two_sequences_bf16_eight_head_groups():
     units = [(b, p, h) for b in range(w.B) for p in pos for h in range(w.Hkv)]
     _check_units(w, inp, (out, lse, sel, None), k, units, "prefill", q_start=0)
 
+
+
+# ------------------------------------------------------------------ heads selecting in smaller groups
+
+@pytest.mark.parametrize("Gs", [1, 2])
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_heads_selecting_in_smaller_groups(Gs, mode):
+    """select_heads = Gs < G: groups of Gs query heads each descend on their own summed logit over
+    their KV head's tree; every group against the oracle's."""
+    w = _w("sel_heads", B=2, Hq=8, Hkv=2, d=128, dtype="bf16", L=16 ** 3 + 100, f=16, k=4, n_queries=3, seed=71)
+    inp = gen_decode_inputs(w)
+    dev = "cuda:0"
+    sh = R.Shape(w.B, w.Hkv, w.Hq, w.d, w.f, w.dtype, w.L, 0.0, w.theta, select_heads=Gs)
+    K, V, W, q = (gpu_util.dev_tensor(inp[x], w.dtype) for x in ("K", "V", "W", "q"))
+    tree = torch.zeros(R.recsa_tree_bytes(sh), dtype=torch.uint8, device=dev)
+    R.recsa_build_tree(sh, K, V, W, 0, w.L, tree)
+    T = R.recsa_num_levels(w.L, w.f)
+    k = [w.k] * T
+    n_q = q.shape[1]
+    groups = w.Hq // Gs
+    q_start = w.L - n_q
+    n_min, n_max = (q_start + 1, w.L) if mode == "prefill" else (w.L, w.L)
+    width = R.recsa_sel_width(sh, n_min, n_max, k)
+    ws = torch.zeros(R.recsa_workspace_bytes(sh, n_max, k), dtype=torch.uint8, device=dev)
+    out = torch.empty(w.B, n_q, w.Hq, w.d, dtype=torch.float32, device=dev)
+    lse = torch.empty(w.B, n_q, w.Hq, dtype=torch.float32, device=dev)
+    sel = torch.full((w.B, n_q, groups, T, width), -7, dtype=torch.int32, device=dev)
+    if mode == "prefill":
+        R.recsa_prefill(sh, q, q_start, K, V, tree, k, out, lse, sel, width, ws)
+        ref = oracle.prefill(inp["K"], inp["V"], inp["W"], inp["q"], q_start, w.f, k, w.dtype, w.theta, select_heads=Gs)
+    else:
+        R.recsa_decode(sh, q, K, V, tree, w.L, k, out, lse, sel, width, ws)
+        ref = oracle.decode(inp["K"], inp["V"], inp["W"], inp["q"], w.L, w.f, k, w.dtype, w.theta, select_heads=Gs)
+    torch.cuda.synchronize()
+    out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
+    stats = {"match": 0, "excused": 0}
+    for (b, j, g), r in ref.items():
+        st = compare_unit(r, sel[b, j, g], out[b, j, g * Gs:(g + 1) * Gs], lse[b, j, g * Gs:(g + 1) * Gs],
+                          TOL[w.dtype], where=f"select_heads {Gs} unit {(b, j, g)}")
+        stats[st] += 1
+    _say(f"select_heads {Gs} {mode}: {stats}")
+    assert stats["match"] >= 0.9 * len(ref)
