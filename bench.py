@@ -555,7 +555,10 @@ def main():
         ms = timed(lambda: R.recsa_prefill(sh, qp, w.L - c, K, V, tree, k, pout, None, None, 0, pws), 3)
         legs["recsa_prefill_last_chunk"] = {"ms_per_call": round(ms, 4), "tokens_per_call": w.B * c,
                                             "tokens_per_s": round(w.B * c / (ms * 1e-3), 1),
-                                            "positions": [w.L - c, w.L]}
+                                            "positions": [w.L - c, w.L],
+                                            # per-unit kernel on the vector ALUs; a position within c
+                                            # of L scores and reads what a query at L does
+                                            "roofline_alu": decode_alu(w, rows, w.B * c, ms)}
         psw = R.recsa_sel_width(sh, w.L - c + 1, w.L, k)
         psel = torch.empty(w.B, c, w.Hkv, len(k), psw, dtype=torch.int32, device=dev)
         R.recsa_prefill(sh, qp, w.L - c, K, V, tree, k, pout, None, psel, psw, pws)
