@@ -104,3 +104,48 @@ def dense_textbook(q, K, V, n_keys, q_pos, theta=1.0e6, scale=None):
     Z = sc * Qr @ Kr.T                     # [G, n]
     lse = logsumexp(Z, axis=1)
     return np.exp(Z - lse[:, None]) @ np.asarray(V[:n_keys], np.float64), lse
+
+
+def brute_two_stage(q, K, V, W, n, f, k_block, k_token, theta=1.0e6, scale=None):
+    """Two-stage block-then-token selection in float64 from its definition: block g (tokens
+    g f .. g f + f - 1) has key W @ mean(its token keys) at position g, the query at the number
+    of blocks; the kept blocks' tokens and the trailing tokens are candidates at their rank, the
+    query at their count; each stage keeps its best k by (-score, position); one softmax over the
+    kept tokens. Returns dict(out, lse, blocks, tokens, gap {1: block gap, 0: token gap})."""
+    q = np.asarray(q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    W = np.asarray(W, np.float64)
+    G, d = q.shape
+    sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    nb = n // f
+    gap = {}
+
+    def pick(S, k):
+        order = sorted(range(len(S)), key=lambda i: (-S[i], i))
+        s = min(k, len(S))
+        if 0 < s < len(S):
+            mx = max(abs(v) for v in S)
+            gap_v = (S[order[s - 1]] - S[order[s]]) / mx if mx > 0 else 0.0
+        else:
+            gap_v = None
+        return sorted(order[:s]), gap_v
+
+    Sb = []
+    for g in range(nb):
+        key = W @ K[g * f:(g + 1) * f].mean(axis=0)
+        Sb.append(sum(sc * np.dot(rot(q[h], nb, theta), rot(key, g, theta)) for h in range(G)))
+    blocks, gap[1] = pick(Sb, k_block)
+    kept = set(blocks)
+    toks = [t for t in range(n) if t >= f * nb or (t // f) in kept]
+    C0 = len(toks)
+    Z = np.array([[sc * np.dot(rot(q[h], C0, theta), rot(K[t], i, theta)) for h in range(G)]
+                  for i, t in enumerate(toks)]).reshape(C0, G)
+    chosen, gap[0] = pick(list(Z.sum(axis=1)), k_token)
+    tokens = [toks[i] for i in chosen]
+    if not chosen:
+        return dict(out=np.zeros((G, d)), lse=np.full(G, -np.inf), blocks=blocks, tokens=tokens, gap=gap)
+    Zk = Z[chosen]                         # [s0, G]
+    lse = logsumexp(Zk, axis=0)
+    out = np.exp(Zk - lse).T @ V[tokens]
+    return dict(out=out, lse=lse, blocks=blocks, tokens=tokens, gap=gap)
