@@ -43,6 +43,9 @@ def parse():
                     help="skip the library flash-attention comparison (torch scaled_dot_product_attention)")
     ap.add_argument("--no-legs", action="store_true", help="skip the dense and prefill comparison legs")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the gradients")
+    ap.add_argument("--no-two-stage", action="store_true", help="skip the two-stage block-then-token variant")
+    ap.add_argument("--ts-blocks", type=int, default=128, help="two-stage variant: blocks kept")
+    ap.add_argument("--ts-tokens", type=int, default=512, help="two-stage variant: tokens kept")
     ap.add_argument("--prefill-chunk", type=int, default=4096)
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step benchmark, sweep the context length (decode 4K-2M, chunked "
@@ -637,6 +640,51 @@ def main():
                          "host_ms_per_step": round(host, 4)}
         res["breakdown"]["generation"] = gen
         del kn, vn, qs, gout
+
+    if not args.no_two_stage:
+        # two-stage block-then-token selection over the same cache and tree: every block (level-1
+        # node) scored, the best ts_blocks kept, their tokens scored, the best ts_tokens attended
+        log("two-stage variant: batched and one-query decode")
+        kb_, kt_ = args.ts_blocks, args.ts_tokens
+        n1 = w.L // w.f
+        s1 = min(kb_, n1)
+        C0 = w.f * s1 + w.L - w.f * n1
+        s0 = min(kt_, C0)
+        bk = torch.empty(w.B, w.Hkv, n1, w.d, dtype=td, device=dev)
+        R.recsa_two_stage_rotate_blocks(sh, tree, 0, w.L, bk)
+        tout = torch.empty_like(out)
+        tws = torch.empty(R.recsa_two_stage_workspace_bytes(sh, w.L, w.n_queries, kb_, kt_), dtype=torch.uint8,
+                          device=dev)
+        ms_rot = timed(lambda: R.recsa_two_stage_decode(sh, q, K, V, tree, w.L, kb_, kt_, tout, workspace=tws), 5)
+        ms_cached = timed(lambda: R.recsa_two_stage_decode(sh, q, K, V, tree, w.L, kb_, kt_, tout, block_keys=bk,
+                                                           workspace=tws), 5)
+        one_q = q[:, :1].contiguous()
+        o1 = torch.empty(w.B, 1, w.Hq, w.d, dtype=torch.float32, device=dev)
+        tws1 = torch.empty(R.recsa_two_stage_workspace_bytes(sh, w.L, 1, kb_, kt_, True), dtype=torch.uint8, device=dev)
+        ms_step = timed(lambda: R.recsa_two_stage_decode(sh, one_q, K, V, tree, w.L, kb_, kt_, o1, block_keys=bk,
+                                                         workspace=tws1), 32)
+        esz = w.elem_bytes
+        block_bytes = w.B * w.Hkv * n1 * w.d * esz               # every block key, once per call
+        tok_bytes_q = w.Hkv * (C0 + s0) * w.d * esz              # per query: candidate key rows + kept value rows
+        flops_q = 2.0 * w.d * w.Hq * n1                          # per query: block logits
+        res["breakdown"]["two_stage"] = {
+            "k_block": kb_, "k_token": kt_, "blocks": n1, "token_candidates": C0, "tokens_kept": s0,
+            "batched": {"ms_per_call": round(ms_rot, 4), "queries_per_call": n_queries,
+                        "queries_per_s": round(n_queries / (ms_rot * 1e-3), 1),
+                        "note": "block keys rotated inside the call"},
+            "batched_rotated_block_cache": {
+                "ms_per_call": round(ms_cached, 4), "queries_per_s": round(n_queries / (ms_cached * 1e-3), 1),
+                "block_TFLOPs": round(flops_q * n_queries / (ms_cached * 1e-3) / 1e12, 1),
+                "token_GBps": round(tok_bytes_q * n_queries / (ms_cached * 1e-3) / 1e9, 1)},
+            "step_rotated_block_cache": {
+                "ms_per_call": round(ms_step, 4), "queries_per_call": w.B,
+                "queries_per_s": round(w.B / (ms_step * 1e-3), 1),
+                "GBps": round((block_bytes + tok_bytes_q * w.B) / (ms_step * 1e-3) / 1e9, 1)},
+            "per_query": {"block_flops": flops_q, "token_bytes": tok_bytes_q}, "block_key_bytes": block_bytes,
+            "speedup_vs_dense_step": (round(res["breakdown"]["legs"]["dense_decode_step"]["ms_per_call"] / ms_step, 2)
+                                      if "legs" in res["breakdown"] else None),
+        }
+        del bk, tout, tws, tws1, o1
 
     if not args.no_backward:
         # gradients with the forward's selections held fixed: the batched decode's 1024 queries,

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define RECSA_ABI_VERSION 2
+#define RECSA_ABI_VERSION 3
 #define RECSA_MAX_LEVELS 32
 
 typedef enum {
@@ -243,6 +243,53 @@ int32_t recsa_distill_step(const recsa_shape_t* shape, const void* q, int64_t n_
                            const void* V, int64_t n_tokens, const int32_t* k_per_level, int32_t n_levels,
                            const float* target, float lr, float* W_master, void* W, void* tree,
                            float* loss, void* workspace, int64_t ws_bytes, void* stream);
+
+/* Two-stage block-then-token selection for decoding, over the same cache and tree: a coarse pass
+ * keeps the best blocks, a token pass keeps the best tokens inside them, and attention runs over
+ * the kept tokens only ["HISA: Efficient Hierarchical Indexing for Fine-Grained Sparse
+ * Attention", summary: block-level filtering, then the token-level indexer inside the kept blocks,
+ * with the same top-k token pattern downstream], with RecSA's pooled keys and index positions
+ * [Abstract, Position]. The pages give no formulas for it. Reading: the blocks are the level-1
+ * nodes (f tokens each, key W @ mean of the token keys, built by recsa_build_tree); with n1 =
+ * floor(n_tokens / f):
+ *   1. every block g < n1 is a candidate at index g, the query at n1; the s1 = min(k_block, n1)
+ *      blocks with the highest group score are kept (ties to the lower index), the rest dropped;
+ *   2. the kept blocks' tokens (ascending), then the trailing tokens f n1 .. n_tokens - 1, are
+ *      candidates at their index i, the query at C0 = f s1 + n_tokens - f n1; the
+ *      s0 = min(k_token, C0) best are kept, the rest dropped;
+ *   3. one softmax per query head over the kept tokens with the logits of step 2.
+ * Scores and logits are those of recsa_decode (same rotation, rounding and scale). Queries as
+ * recsa_decode: n_q per sequence, all at position n_tokens, not in the cache. select_heads must
+ * be 0 (or G).
+ *   q [dev]: [B][n_q][H_q][d]; K, V [dev]: caches; tree [dev]: built up to n_tokens (level 1 is read).
+ *   block_keys [dev] (nullable): [B][H_kv][floor(capacity / f)][d] storage type, the level-1 keys
+ *   rotated at their block index (recsa_two_stage_rotate_blocks), valid for every block below n1;
+ *   NULL rotates them into the workspace on every call.
+ *   out [dev]: float32 [B][n_q][H_q][d]; lse [dev] (nullable): float32 [B][n_q][H_q] (-inf and out = 0
+ *   when nothing is kept).
+ *   sel_blocks [dev] (nullable): int32 [B][n_q][H_kv][sel_block_width], kept block ids ascending,
+ *   -1 padded, sel_block_width >= s1; sel_tokens [dev] (nullable): int32 [B][n_q][H_kv][sel_token_width],
+ *   kept token ids ascending, -1 padded, sel_token_width >= s0.
+ *   workspace: recsa_two_stage_workspace_bytes(shape, n_tokens, n_q, k_block, k_token,
+ *   block_keys != NULL): RoPE table, rotated queries, rotated block keys (when not given) and the
+ *   per-slab candidate lists.
+ * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED (select_heads, or k_block / k_token so large that a
+ * query's candidate lists exceed on-chip memory), WORKSPACE. */
+int64_t recsa_two_stage_workspace_bytes(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q, int32_t k_block,
+                                        int32_t k_token, int32_t blocks_rotated);
+int32_t recsa_two_stage_decode(const recsa_shape_t* shape, const void* q, int64_t n_q, const void* K, const void* V,
+                               const void* tree, const void* block_keys, int64_t n_tokens, int32_t k_block,
+                               int32_t k_token, float* out, float* lse, int32_t* sel_blocks, int32_t sel_block_width,
+                               int32_t* sel_tokens, int32_t sel_token_width, void* workspace, int64_t ws_bytes,
+                               void* stream);
+
+/* Rotates the level-1 keys of the blocks complete at n_new but not at n_old into block_keys
+ * (block g at position g, recsa_rotate_keys' arithmetic): a cache of rotated block keys kept next
+ * to the tree, for recsa_two_stage_decode.
+ *   tree [dev]: built up to n_new; block_keys [dev]: [B][H_kv][floor(capacity / f)][d] storage type.
+ * Errors: INVALID_ARG (null, misaligned, overlap, n_old > n_new), CAPACITY. */
+int32_t recsa_two_stage_rotate_blocks(const recsa_shape_t* shape, const void* tree, int64_t n_old, int64_t n_new,
+                                      void* block_keys, void* stream);
 
 /* Dense softmax attention with standard RoPE at the original positions -- the comparator the
  * method is timed against [Abstract]; also RecSA's limit when every level keeps everything.

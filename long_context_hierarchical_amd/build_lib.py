@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "librecsa.so")
-SOURCES = ["build_tree.hip", "step.hip", "attend.hip", "backward.hip", "distill.hip", "dense.hip", "api.cpp"]
+SOURCES = ["build_tree.hip", "step.hip", "attend.hip", "backward.hip", "distill.hip", "dense.hip", "two_stage.hip", "api.cpp"]
 # HBM read/copy probe (a separate program, not part of the library): the achievable bandwidth
 PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
 PROBE = os.path.join(PKG, "probe", "hbm_probe")

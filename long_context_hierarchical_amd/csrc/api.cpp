@@ -757,6 +757,162 @@ int32_t recsa_rotate_keys(const recsa_shape_t* shape, const void* K, int64_t n_t
   return RECSA_OK;
 }
 
+// ---------------------------------------------------------------- two-stage block-then-token selection
+
+struct TsPlan {
+  Info I;
+  int64_t n1 = 0, s1 = 0, C0 = 0, s0 = 0, SB = 0, n_slabs = 0, merge = 0;
+  int64_t tab_bytes = 0, q_bytes = 0, kb_bytes = 0, cand_bytes = 0, total = 0;
+  size_t lds = 0;
+};
+
+static int32_t ts_plan(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q, int32_t k_block, int32_t k_token,
+                       bool own_blocks, TsPlan* p) {
+  Info& I = p->I;
+  int32_t rc = check_shape(shape, &I);
+  if (rc) return rc;
+  rc = need_group_selection(I);
+  if (rc) return rc;
+  if (n_tokens < 0 || n_q < 0) return fail(RECSA_ERR_INVALID_ARG, "n_tokens and n_q must be >= 0");
+  if (k_block < 0 || k_token < 0) return fail(RECSA_ERR_INVALID_ARG, "k_block and k_token must be >= 0");
+  if (n_tokens > I.cap) return fail(RECSA_ERR_CAPACITY, "n_tokens %lld exceeds the capacity %lld", (long long)n_tokens,
+                                    (long long)I.cap);
+  if (n_q > INT32_MAX || I.B * I.Hkv > 65535) return fail(RECSA_ERR_UNSUPPORTED, "grid too large");
+  p->n1 = n_tokens / I.f;
+  p->s1 = std::min<int64_t>(k_block, p->n1);
+  p->C0 = I.f * p->s1 + (n_tokens - I.f * p->n1);
+  p->s0 = std::min<int64_t>(k_token, p->C0);
+  p->SB = recsa::ts_slab_blocks(static_cast<int>(I.G), I.bf16);
+  p->n_slabs = (p->n1 + p->SB - 1) / p->SB;
+  for (int64_t t = 0; t < p->n_slabs; ++t) p->merge += std::min<int64_t>(p->s1, std::min<int64_t>(p->SB, p->n1 - t * p->SB));
+  const recsa::TsTokenLayout L = recsa::ts_token_layout(static_cast<int>(I.d), static_cast<int>(I.G), p->merge, p->C0,
+                                                        p->s1, p->s0);
+  p->lds = static_cast<size_t>(L.total);
+  if (p->lds > kMaxLds)
+    return fail(RECSA_ERR_UNSUPPORTED,
+                "k_block = %d and k_token = %d need %zu bytes of LDS per query (max %zu): %lld token candidates, "
+                "%lld merged blocks",
+                k_block, k_token, p->lds, kMaxLds, (long long)p->C0, (long long)p->merge);
+  p->tab_bytes = p->C0 > 0 ? table_bytes(I, p->C0) : 0;
+  p->q_bytes = al256(I.B * n_q * I.Hq * I.d * I.esz);
+  p->kb_bytes = own_blocks && p->s1 > 0 ? al256(I.B * I.Hkv * p->n1 * I.d * I.esz) : 0;
+  p->cand_bytes = p->s1 > 0 ? al256(I.B * I.Hkv * n_q * p->n_slabs * p->s1 * 8) : 0;
+  p->total = p->tab_bytes + 2 * p->q_bytes + p->kb_bytes + p->cand_bytes;
+  return RECSA_OK;
+}
+
+int64_t recsa_two_stage_workspace_bytes(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q, int32_t k_block,
+                                        int32_t k_token, int32_t blocks_rotated) {
+  TsPlan p;
+  if (ts_plan(shape, n_tokens, n_q, k_block, k_token, blocks_rotated == 0, &p)) return -1;
+  return p.total;
+}
+
+int32_t recsa_two_stage_rotate_blocks(const recsa_shape_t* shape, const void* tree, int64_t n_old, int64_t n_new,
+                                      void* block_keys, void* stream) {
+  Info I;
+  int32_t rc = check_shape(shape, &I);
+  if (rc) return rc;
+  if (n_old < 0 || n_new < n_old) return fail(RECSA_ERR_INVALID_ARG, "need 0 <= n_old <= n_new");
+  if (n_new > I.cap) return fail(RECSA_ERR_CAPACITY, "n_new %lld exceeds the capacity %lld", (long long)n_new,
+                                 (long long)I.cap);
+  const int64_t lo = n_old / I.f, hi = n_new / I.f;
+  if (hi <= lo) return RECSA_OK;
+  if (!tree || !block_keys) return fail(RECSA_ERR_INVALID_ARG, "tree or block_keys is NULL");
+  if (!aligned16(tree) || !aligned16(block_keys)) return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const int64_t rows = nodes_at(I.cap, I.f, 1);
+  const char* nk = static_cast<const char*>(tree) + level_offset_bytes(I, 1, 0);
+  const int64_t bytes = I.B * I.Hkv * rows * I.d * I.esz;
+  const char* bk = static_cast<const char*>(block_keys);
+  if (nk < bk + bytes && bk < nk + bytes) return fail(RECSA_ERR_INVALID_ARG, "block_keys overlaps the tree's block keys");
+  hipError_t e = recsa::launch_rotate_keys(nk, rows, block_keys, rows, hi, I.B * I.Hkv, static_cast<int>(I.d), I.bf16,
+                                           inv_freq_of(I), I.theta != 0.0f, static_cast<hipStream_t>(stream), lo);
+  if (e != hipSuccess) return hip_fail(e, "block key rotation launch");
+  return RECSA_OK;
+}
+
+int32_t recsa_two_stage_decode(const recsa_shape_t* shape, const void* q, int64_t n_q, const void* K, const void* V,
+                               const void* tree, const void* block_keys, int64_t n_tokens, int32_t k_block,
+                               int32_t k_token, float* out, float* lse, int32_t* sel_blocks, int32_t sel_block_width,
+                               int32_t* sel_tokens, int32_t sel_token_width, void* workspace, int64_t ws_bytes,
+                               void* stream) {
+  TsPlan p;
+  int32_t rc = ts_plan(shape, n_tokens, n_q, k_block, k_token, block_keys == nullptr, &p);
+  if (rc) return rc;
+  const Info& I = p.I;
+  if (n_q == 0) return RECSA_OK;
+  if (!q || !out || (n_tokens > 0 && (!K || !V)) || (p.n1 > 0 && !tree))
+    return fail(RECSA_ERR_INVALID_ARG, "q, K, V, tree or out is NULL");
+  if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(tree) || !aligned16(block_keys) ||
+      !aligned16(out) || !aligned16(workspace))
+    return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  if (sel_blocks && sel_block_width < p.s1)
+    return fail(RECSA_ERR_INVALID_ARG, "sel_block_width %d < %lld kept blocks", sel_block_width, (long long)p.s1);
+  if (sel_tokens && sel_token_width < p.s0)
+    return fail(RECSA_ERR_INVALID_ARG, "sel_token_width %d < %lld kept tokens", sel_token_width, (long long)p.s0);
+  if (ws_bytes < p.total) return fail(RECSA_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)ws_bytes,
+                                      (long long)p.total);
+  if (p.total > 0 && !workspace) return fail(RECSA_ERR_INVALID_ARG, "workspace is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const recsa::InvFreq iv = inv_freq_of(I);
+  const int use_rope = I.theta != 0.0f;
+  recsa::TsArgs a{};
+  a.tab = p.tab_bytes > 0 ? reinterpret_cast<const float2*>(ws) : nullptr;
+  char* q1 = ws + p.tab_bytes;
+  char* q0 = q1 + p.q_bytes;
+  a.q1 = q1;
+  a.q0 = q0;
+  a.kb = block_keys ? block_keys : static_cast<const void*>(q0 + p.q_bytes);
+  a.kb_rows = block_keys ? nodes_at(I.cap, I.f, 1) : p.n1;
+  a.cand = reinterpret_cast<uint2*>(q0 + p.q_bytes + p.kb_bytes);
+  a.K = K;
+  a.V = V;
+  a.cap = I.cap;
+  a.out = out;
+  a.lse = lse;
+  a.sel_blocks = sel_blocks;
+  a.sel_tokens = sel_tokens;
+  a.sel_bw = sel_blocks ? sel_block_width : 0;
+  a.sel_tw = sel_tokens ? sel_token_width : 0;
+  a.n = n_tokens;
+  a.n1 = p.n1;
+  a.n_q = n_q;
+  a.BH = I.B * I.Hkv;
+  a.Hkv = static_cast<int32_t>(I.Hkv);
+  a.Hq = static_cast<int32_t>(I.Hq);
+  a.f = static_cast<int32_t>(I.f);
+  a.s1 = static_cast<int32_t>(p.s1);
+  a.C0 = static_cast<int32_t>(p.C0);
+  a.s0 = static_cast<int32_t>(p.s0);
+  a.SB = static_cast<int32_t>(p.SB);
+  a.n_slabs = static_cast<int32_t>(p.n_slabs);
+  a.merge = static_cast<int32_t>(p.merge);
+  a.use_rope = use_rope && p.C0 > 0;
+  a.scale = I.scale;
+  hipError_t e;
+  if (a.tab) {
+    e = recsa::launch_rope_table(reinterpret_cast<float2*>(ws), p.C0, static_cast<int>(I.d / 2), iv, st);
+    if (e != hipSuccess) return hip_fail(e, "RoPE table launch");
+  }
+  e = recsa::launch_ts_rotate_queries(q, q1, q0, I.B * n_q * I.Hq, p.n1, p.C0, static_cast<int>(I.d), I.bf16, iv,
+                                      use_rope, st);
+  if (e != hipSuccess) return hip_fail(e, "query rotation launch");
+  if (p.s1 > 0) {
+    if (!block_keys) {
+      e = recsa::launch_rotate_keys(static_cast<const char*>(tree) + level_offset_bytes(I, 1, 0), nodes_at(I.cap, I.f, 1),
+                                    q0 + p.q_bytes, p.n1, p.n1, I.B * I.Hkv, static_cast<int>(I.d), I.bf16, iv, use_rope,
+                                    st);
+      if (e != hipSuccess) return hip_fail(e, "block key rotation launch");
+    }
+    e = recsa::launch_ts_score(a, static_cast<int>(I.d), I.bf16, static_cast<int>(I.G), st);
+    if (e != hipSuccess) return hip_fail(e, "block scoring launch");
+  }
+  e = recsa::launch_ts_tokens(a, static_cast<int>(I.d), I.bf16, static_cast<int>(I.G), p.lds, I.B, st);
+  if (e != hipSuccess) return hip_fail(e, "token stage launch");
+  return RECSA_OK;
+}
+
 int32_t recsa_dense_ref_attn(const recsa_shape_t* shape, const void* q, int64_t q_start, int64_t n_q, const void* K,
                              const void* V, int64_t n_tokens, int32_t mode, float* out, float* lse, void* workspace,
                              int64_t ws_bytes, void* stream) {

@@ -35,24 +35,18 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
 }
 
-__device__ __forceinline__ void rope_cs(int64_t p, float w, float& c, float& s) {
-  double sd, cd;
-  sincos(static_cast<double>(p) * static_cast<double>(w), &sd, &cd);
-  c = static_cast<float>(cd);
-  s = static_cast<float>(sd);
-}
-
 // ---------------------------------------------------------------- key rotation
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void rotate_keys_kernel(const void* K, int64_t cap, void* Kr, int64_t kr_rows,
-                                                          int64_t n, int64_t BH, InvFreq iv, int use_rope) {
+                                                          int64_t p_lo, int64_t n, int64_t BH, InvFreq iv, int use_rope) {
   constexpr int HALF = D / 2, CPR = HALF / 8;
+  const int64_t rows = n - p_lo;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= BH * n * CPR) return;
+  if (idx >= BH * rows * CPR) return;
   const int c = static_cast<int>(idx % CPR);
   const int64_t row = idx / CPR;
-  const int64_t bh = row / n, p = row % n;
+  const int64_t bh = row / rows, p = p_lo + row % rows;
   const int64_t src = (bh * cap + p) * D, dst = (bh * kr_rows + p) * D;
   float lo[8], hi[8], olo[8], ohi[8];
   load8<BF16>(K, src + 8 * c, lo);
@@ -75,16 +69,16 @@ __global__ __launch_bounds__(256) void rotate_keys_kernel(const void* K, int64_t
 }
 
 hipError_t launch_rotate_keys(const void* K, int64_t cap, void* Kr, int64_t kr_rows, int64_t n, int64_t BH, int d,
-                              bool bf16, const InvFreq& iv, int use_rope, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const int64_t total = BH * n * (d / 16);
+                              bool bf16, const InvFreq& iv, int use_rope, hipStream_t s, int64_t p_lo) {
+  if (n <= p_lo) return hipSuccess;
+  const int64_t total = BH * (n - p_lo) * (d / 16);
   const dim3 grid(static_cast<unsigned>((total + 255) / 256));
   if (d == 128) {
-    if (bf16) hipLaunchKernelGGL((rotate_keys_kernel<128, true>), grid, dim3(256), 0, s, K, cap, Kr, kr_rows, n, BH, iv, use_rope);
-    else hipLaunchKernelGGL((rotate_keys_kernel<128, false>), grid, dim3(256), 0, s, K, cap, Kr, kr_rows, n, BH, iv, use_rope);
+    if (bf16) hipLaunchKernelGGL((rotate_keys_kernel<128, true>), grid, dim3(256), 0, s, K, cap, Kr, kr_rows, p_lo, n, BH, iv, use_rope);
+    else hipLaunchKernelGGL((rotate_keys_kernel<128, false>), grid, dim3(256), 0, s, K, cap, Kr, kr_rows, p_lo, n, BH, iv, use_rope);
   } else {
-    if (bf16) hipLaunchKernelGGL((rotate_keys_kernel<64, true>), grid, dim3(256), 0, s, K, cap, Kr, kr_rows, n, BH, iv, use_rope);
-    else hipLaunchKernelGGL((rotate_keys_kernel<64, false>), grid, dim3(256), 0, s, K, cap, Kr, kr_rows, n, BH, iv, use_rope);
+    if (bf16) hipLaunchKernelGGL((rotate_keys_kernel<64, true>), grid, dim3(256), 0, s, K, cap, Kr, kr_rows, p_lo, n, BH, iv, use_rope);
+    else hipLaunchKernelGGL((rotate_keys_kernel<64, false>), grid, dim3(256), 0, s, K, cap, Kr, kr_rows, p_lo, n, BH, iv, use_rope);
   }
   return hipGetLastError();
 }

@@ -166,10 +166,10 @@ hipError_t launch_distill_loss(const float* out, const float* target, float* dou
 hipError_t launch_distill_update(float* Wm, const float* dW, void* W, float lr, int64_t n, bool bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- dense reference attention
-// Keys rotated at their own positions: Kr[bh][p] = round(rot(K[bh][p], p)), p < n
+// Keys rotated at their own positions: Kr[bh][p] = round(rot(K[bh][p], p)), p_lo <= p < n
 // (K rows per slice: cap; Kr rows per slice: kr_rows).
 hipError_t launch_rotate_keys(const void* K, int64_t cap, void* Kr, int64_t kr_rows, int64_t n, int64_t BH, int d,
-                              bool bf16, const InvFreq& iv, int use_rope, hipStream_t s);
+                              bool bf16, const InvFreq& iv, int use_rope, hipStream_t s, int64_t p_lo = 0);
 
 struct DenseArgs {
   const void* q;        // [B][n_q][H_q][d]
@@ -195,5 +195,82 @@ hipError_t launch_dense(const DenseArgs& a, int d, bool bf16, int G, int64_t B, 
 // bf16 queries rotated at their positions into qr ([B][n_q][H_q][d], bf16), for the MFMA kernel.
 hipError_t launch_rotate_queries(const DenseArgs& a, void* qr, int64_t B, int d, hipStream_t s);
 hipError_t launch_attend(const AttnArgs& a, int d, bool bf16, int G, size_t lds, int64_t B, hipStream_t s);
+
+// ---------------------------------------------------------------- two-stage block-then-token selection
+// Stage 1 scores every complete block (level-1 node) of a slice for every query and keeps, per
+// slab of SB blocks, the slab's best s1c = min(s1, blocks in the slab) as (ordered score bits,
+// block id) in ascending block order. Stage 2, one workgroup per (query, KV head), merges the
+// slabs' lists into the s1 kept blocks, scores their tokens and the trailing tokens, keeps the
+// best s0 and takes one softmax over them.
+struct TsArgs {
+  const void* q1;       // queries rotated at n1 [B][n_q][H_q][d], storage type
+  const void* q0;       // queries rotated at C0
+  const void* kb;       // block keys rotated at their index [BH][kb_rows][d]
+  int64_t kb_rows;
+  const void* K;        // token rows [BH][cap][d], pre-RoPE
+  const void* V;
+  int64_t cap;
+  uint2* cand;          // [BH][n_q][n_slabs][s1] (ordered score bits, block id)
+  const float2* tab;    // RoPE table rows 0..C0, or null without rotation
+  float* out;           // [B][n_q][H_q][d]
+  float* lse;           // [B][n_q][H_q] or null
+  int32_t* sel_blocks;  // [B][n_q][H_kv][sel_bw] or null
+  int32_t* sel_tokens;  // [B][n_q][H_kv][sel_tw] or null
+  int32_t sel_bw, sel_tw;
+  int64_t n;            // visible tokens
+  int64_t n1;           // complete blocks, floor(n / f)
+  int64_t n_q;
+  int64_t BH;
+  int32_t Hkv, Hq, f;
+  int32_t s1;           // blocks kept, min(k_block, n1)
+  int32_t C0;           // token candidates, f s1 + n - f n1
+  int32_t s0;           // tokens kept, min(k_token, C0)
+  int32_t SB, n_slabs;  // blocks per slab of stage 1, slabs
+  int32_t merge;        // entries of the merged list, sum over slabs of s1c
+  int32_t use_rope;
+  float scale;
+};
+
+// Blocks per stage-1 slab (a multiple of 128).
+__host__ __device__ constexpr int ts_slab_blocks(int G, bool bf16) {
+  return ((bf16 ? 15360 : 10240) / (32 / G)) / 128 * 128;
+}
+
+// Byte offsets of the stage-2 workgroup's LDS regions. The merged block list (scores, ids) and
+// the token logits and scores share the first region: the list is consumed before any token is
+// scored.
+struct TsTokenLayout {
+  int64_t mk, mg, zs, keys, kb, kp, qs, red, hist, total;
+};
+__host__ __device__ inline int64_t ts_al16(int64_t x) { return (x + 15) / 16 * 16; }
+__host__ __device__ inline TsTokenLayout ts_token_layout(int d, int G, int64_t merge, int64_t C0, int64_t s1,
+                                                        int64_t s0) {
+  TsTokenLayout L{};
+  L.mk = 0;
+  L.mg = ts_al16(merge * 4);
+  L.zs = 0;
+  L.keys = ts_al16(C0 * G * 4);
+  const int64_t tok = L.keys + ts_al16(C0 * 4), mrg = 2 * ts_al16(merge * 4);
+  int64_t off = tok > mrg ? tok : mrg;
+  L.kb = off;
+  off += ts_al16(s1 * 4);
+  L.kp = off;
+  off += ts_al16(s0 * 4);
+  L.qs = off;
+  off += ts_al16(static_cast<int64_t>(G) * d * 4);
+  L.red = off;
+  off += ts_al16(4 * static_cast<int64_t>(G) * d * 4);
+  L.hist = off;
+  off += 256 * 4;
+  L.total = off;
+  return L;
+}
+
+// q1[row] = round(rot(q[row], p1)), q0[row] = round(rot(q[row], p0)) for rows = B n_q H_q (copies
+// without rotation).
+hipError_t launch_ts_rotate_queries(const void* q, void* q1, void* q0, int64_t rows, int64_t p1, int64_t p0, int d,
+                                    bool bf16, const InvFreq& iv, int use_rope, hipStream_t s);
+hipError_t launch_ts_score(const TsArgs& a, int d, bool bf16, int G, hipStream_t s);
+hipError_t launch_ts_tokens(const TsArgs& a, int d, bool bf16, int G, size_t lds, int64_t B, hipStream_t s);
 
 }  // namespace recsa

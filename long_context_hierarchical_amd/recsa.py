@@ -24,6 +24,7 @@ EXPORTS = (
     "recsa_decode_step", "recsa_backward_workspace_bytes", "recsa_backward", "recsa_distill_workspace_bytes",
     "recsa_distill_step",
     "recsa_dense_workspace_bytes", "recsa_dense_ref_attn", "recsa_rotate_keys",
+    "recsa_two_stage_workspace_bytes", "recsa_two_stage_decode", "recsa_two_stage_rotate_blocks",
 )
 RECSA_DENSE_CAUSAL, RECSA_DENSE_KEYS_ROTATED = 1, 2
 
@@ -98,6 +99,10 @@ def lib() -> ctypes.CDLL:
             "recsa_dense_workspace_bytes": (I64, [SP, I64, I64, I32]),
             "recsa_dense_ref_attn": (I32, [SP, P, I64, I64, P, P, I64, I32, P, P, P, I64, P]),
             "recsa_rotate_keys": (I32, [SP, P, I64, P, P]),
+            "recsa_two_stage_workspace_bytes": (I64, [SP, I64, I64, I32, I32, I32]),
+            "recsa_two_stage_decode": (I32, [SP, P, I64, P, P, P, P, I64, I32, I32, P, P, P, I32, P, I32, P, I64,
+                                             P]),
+            "recsa_two_stage_rotate_blocks": (I32, [SP, P, I64, I64, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -239,6 +244,28 @@ def recsa_dense_ref_attn(shape: Shape, q, q_start: int, K, V, n_tokens: int, mod
 
 def recsa_rotate_keys(shape: Shape, K, n_tokens: int, K_rot, stream=None):
     _check(lib().recsa_rotate_keys(ctypes.byref(shape.c()), _p(K), n_tokens, _p(K_rot), _stream(stream)))
+
+
+def recsa_two_stage_workspace_bytes(shape: Shape, n_tokens: int, n_q: int, k_block: int, k_token: int,
+                                    blocks_rotated: bool = False) -> int:
+    return _nbytes(lib().recsa_two_stage_workspace_bytes(ctypes.byref(shape.c()), n_tokens, n_q, int(k_block),
+                                                         int(k_token), 1 if blocks_rotated else 0))
+
+
+def recsa_two_stage_decode(shape: Shape, q, K, V, tree, n_tokens: int, k_block: int, k_token: int, out, lse=None,
+                           sel_blocks=None, sel_tokens=None, block_keys=None, workspace=None, stream=None):
+    n_q = q.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    bw = 0 if sel_blocks is None else sel_blocks.shape[-1]
+    tw = 0 if sel_tokens is None else sel_tokens.shape[-1]
+    _check(lib().recsa_two_stage_decode(ctypes.byref(shape.c()), _p(q), n_q, _p(K), _p(V), _p(tree), _p(block_keys),
+                                        n_tokens, int(k_block), int(k_token), _p(out), _p(lse), _p(sel_blocks), bw,
+                                        _p(sel_tokens), tw, _p(workspace), ws_bytes, _stream(stream)))
+
+
+def recsa_two_stage_rotate_blocks(shape: Shape, tree, n_old: int, n_new: int, block_keys, stream=None):
+    _check(lib().recsa_two_stage_rotate_blocks(ctypes.byref(shape.c()), _p(tree), n_old, n_new, _p(block_keys),
+                                               _stream(stream)))
 
 
 # ----------------------------------------------------------------- views

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(R.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert R.recsa_abi_version() == 2
+    assert R.recsa_abi_version() == 3
 
 
 def _shape(**kw):
@@ -153,3 +153,42 @@ def test_error_paths_return_status_before_launch():
     assert _status(bwd, alone, False, q, 0, 4096, *args, workspace=t, stream=ns) == -3
     assert _status(R.recsa_decode, _shape(capacity=4096, select_heads=3), q, t, t, t, 4096, k, t, None, None, 0, t,
                    ns) == -1
+
+
+def test_two_stage_sizes_and_error_paths():
+    """Workspace = RoPE table (rows 0..C0) + queries rotated at two positions + rotated block keys
+    (unless given) + the per-slab candidate lists; bad arguments are rejected before any launch."""
+    sh = _shape(batch=4, capacity=1 << 19)
+    n, nq, kb, kt = 1 << 19, 256, 128, 512
+    n1 = n // 16
+    C0 = 16 * kb
+    SB = 1920                                   # blocks per slab for 4 query heads per KV head, bf16
+    slabs = -(-n1 // SB)
+    al = lambda x: (x + 255) // 256 * 256
+    want = (al((C0 + 1) * 64 * 8) + 2 * al(4 * nq * 32 * 128 * 2) + al(4 * 8 * n1 * 128 * 2)
+            + al(4 * 8 * nq * slabs * kb * 8))
+    assert R.recsa_two_stage_workspace_bytes(sh, n, nq, kb, kt) == want
+    assert R.recsa_two_stage_workspace_bytes(sh, n, nq, kb, kt, blocks_rotated=True) == want - al(4 * 8 * n1 * 128 * 2)
+    t = _FakeTensor()
+    ns = _NoStream()
+    q = _FakeTensor(shape=(4, nq, 32, 128))
+    ts = R.recsa_two_stage_decode
+    assert _status(ts, sh, q, t, t, t, n + 1, kb, kt, t, workspace=t, stream=ns) == -2
+    assert _status(ts, sh, q, t, t, t, n, -1, kt, t, workspace=t, stream=ns) == -1
+    assert _status(ts, sh, q, t, t, t, n, kb, -1, t, workspace=t, stream=ns) == -1
+    assert _status(ts, _shape(batch=4, capacity=n, select_heads=1), q, t, t, t, n, kb, kt, t, workspace=t,
+                   stream=ns) == -3
+    assert _status(ts, sh, q, t, t, t, n, 4096, kt, t, workspace=t, stream=ns) == -3        # lists beyond LDS
+    sb = _FakeTensor(shape=(4, nq, 8, kb - 1))
+    assert _status(ts, sh, q, t, t, t, n, kb, kt, t, sel_blocks=sb, workspace=t, stream=ns) == -1
+    st = _FakeTensor(shape=(4, nq, 8, kt - 1))
+    assert _status(ts, sh, q, t, t, t, n, kb, kt, t, sel_tokens=st, workspace=t, stream=ns) == -1
+    small_ws = _FakeTensor()
+    small_ws.numel = lambda: 1024
+    assert _status(ts, sh, q, t, t, t, n, kb, kt, t, workspace=small_ws, stream=ns) == -5
+    assert _status(ts, sh, q, None, t, t, n, kb, kt, t, workspace=t, stream=ns) == -1
+    rb = R.recsa_two_stage_rotate_blocks
+    assert _status(rb, sh, t, 10, 5, t, ns) == -1
+    assert _status(rb, sh, t, 0, n + 16, t, ns) == -2
+    assert _status(rb, sh, None, 0, 4096, t, ns) == -1
+    assert _status(rb, sh, t, 0, 4096, t, ns) == -1                                        # block_keys = tree
