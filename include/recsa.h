@@ -271,8 +271,8 @@ int32_t recsa_distill_step(const recsa_shape_t* shape, const void* q, int64_t n_
  *   -1 padded, sel_block_width >= s1; sel_tokens [dev] (nullable): int32 [B][n_q][H_kv][sel_token_width],
  *   kept token ids ascending, -1 padded, sel_token_width >= s0.
  *   workspace: recsa_two_stage_workspace_bytes(shape, n_tokens, n_q, k_block, k_token,
- *   block_keys != NULL): RoPE table, rotated queries, rotated block keys (when not given) and the
- *   per-slab candidate lists.
+ *   block_keys != NULL): RoPE table, rotated queries, rotated block keys (when not given), the
+ *   per-slab candidate lists and the kept block ids.
  * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED (select_heads, or k_block / k_token so large that a
  * query's candidate lists exceed on-chip memory), WORKSPACE. */
 int64_t recsa_two_stage_workspace_bytes(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q, int32_t k_block,

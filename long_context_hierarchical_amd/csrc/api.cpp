@@ -762,7 +762,7 @@ int32_t recsa_rotate_keys(const recsa_shape_t* shape, const void* K, int64_t n_t
 struct TsPlan {
   Info I;
   int64_t n1 = 0, s1 = 0, C0 = 0, s0 = 0, SB = 0, n_slabs = 0, merge = 0;
-  int64_t tab_bytes = 0, q_bytes = 0, kb_bytes = 0, cand_bytes = 0, total = 0;
+  int64_t tab_bytes = 0, q_bytes = 0, kb_bytes = 0, cand_bytes = 0, kept_bytes = 0, total = 0;
   size_t lds = 0;
 };
 
@@ -782,12 +782,12 @@ static int32_t ts_plan(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q
   p->s1 = std::min<int64_t>(k_block, p->n1);
   p->C0 = I.f * p->s1 + (n_tokens - I.f * p->n1);
   p->s0 = std::min<int64_t>(k_token, p->C0);
-  p->SB = recsa::ts_slab_blocks(static_cast<int>(I.G), I.bf16);
+  p->SB = recsa::ts_slab_blocks(static_cast<int>(I.G));
   p->n_slabs = (p->n1 + p->SB - 1) / p->SB;
   for (int64_t t = 0; t < p->n_slabs; ++t) p->merge += std::min<int64_t>(p->s1, std::min<int64_t>(p->SB, p->n1 - t * p->SB));
-  const recsa::TsTokenLayout L = recsa::ts_token_layout(static_cast<int>(I.d), static_cast<int>(I.G), p->merge, p->C0,
-                                                        p->s1, p->s0);
-  p->lds = static_cast<size_t>(L.total);
+  const recsa::TsTokenLayout L = recsa::ts_token_layout(static_cast<int>(I.d), static_cast<int>(I.G), p->C0, p->s1,
+                                                        p->s0);
+  p->lds = std::max(static_cast<size_t>(L.total), recsa::ts_merge_lds_bytes(p->merge));
   if (p->lds > kMaxLds)
     return fail(RECSA_ERR_UNSUPPORTED,
                 "k_block = %d and k_token = %d need %zu bytes of LDS per query (max %zu): %lld token candidates, "
@@ -797,7 +797,8 @@ static int32_t ts_plan(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q
   p->q_bytes = al256(I.B * n_q * I.Hq * I.d * I.esz);
   p->kb_bytes = own_blocks && p->s1 > 0 ? al256(I.B * I.Hkv * p->n1 * I.d * I.esz) : 0;
   p->cand_bytes = p->s1 > 0 ? al256(I.B * I.Hkv * n_q * p->n_slabs * p->s1 * 8) : 0;
-  p->total = p->tab_bytes + 2 * p->q_bytes + p->kb_bytes + p->cand_bytes;
+  p->kept_bytes = p->s1 > 0 ? al256(I.B * I.Hkv * n_q * p->s1 * 4) : 0;
+  p->total = p->tab_bytes + 2 * p->q_bytes + p->kb_bytes + p->cand_bytes + p->kept_bytes;
   return RECSA_OK;
 }
 
@@ -866,6 +867,7 @@ int32_t recsa_two_stage_decode(const recsa_shape_t* shape, const void* q, int64_
   a.kb = block_keys ? block_keys : static_cast<const void*>(q0 + p.q_bytes);
   a.kb_rows = block_keys ? nodes_at(I.cap, I.f, 1) : p.n1;
   a.cand = reinterpret_cast<uint2*>(q0 + p.q_bytes + p.kb_bytes);
+  a.kept = reinterpret_cast<int32_t*>(q0 + p.q_bytes + p.kb_bytes + p.cand_bytes);
   a.K = K;
   a.V = V;
   a.cap = I.cap;
@@ -907,6 +909,8 @@ int32_t recsa_two_stage_decode(const recsa_shape_t* shape, const void* q, int64_
     }
     e = recsa::launch_ts_score(a, static_cast<int>(I.d), I.bf16, static_cast<int>(I.G), st);
     if (e != hipSuccess) return hip_fail(e, "block scoring launch");
+    e = recsa::launch_ts_merge(a, st);
+    if (e != hipSuccess) return hip_fail(e, "block merge launch");
   }
   e = recsa::launch_ts_tokens(a, static_cast<int>(I.d), I.bf16, static_cast<int>(I.G), p.lds, I.B, st);
   if (e != hipSuccess) return hip_fail(e, "token stage launch");

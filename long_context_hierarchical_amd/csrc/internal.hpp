@@ -200,8 +200,8 @@ hipError_t launch_attend(const AttnArgs& a, int d, bool bf16, int G, size_t lds,
 // Stage 1 scores every complete block (level-1 node) of a slice for every query and keeps, per
 // slab of SB blocks, the slab's best s1c = min(s1, blocks in the slab) as (ordered score bits,
 // block id) in ascending block order. Stage 2, one workgroup per (query, KV head), merges the
-// slabs' lists into the s1 kept blocks, scores their tokens and the trailing tokens, keeps the
-// best s0 and takes one softmax over them.
+// slabs' lists into the s1 kept blocks, then scores their tokens and the trailing tokens, keeps
+// the best s0 and takes one softmax over them.
 struct TsArgs {
   const void* q1;       // queries rotated at n1 [B][n_q][H_q][d], storage type
   const void* q0;       // queries rotated at C0
@@ -211,6 +211,7 @@ struct TsArgs {
   const void* V;
   int64_t cap;
   uint2* cand;          // [BH][n_q][n_slabs][s1] (ordered score bits, block id)
+  int32_t* kept;        // [BH][n_q][s1] kept block ids, ascending
   const float2* tab;    // RoPE table rows 0..C0, or null without rotation
   float* out;           // [B][n_q][H_q][d]
   float* lse;           // [B][n_q][H_q] or null
@@ -231,46 +232,43 @@ struct TsArgs {
   float scale;
 };
 
-// Blocks per stage-1 slab (a multiple of 128).
-__host__ __device__ constexpr int ts_slab_blocks(int G, bool bf16) {
-  return ((bf16 ? 15360 : 10240) / (32 / G)) / 128 * 128;
-}
+// Blocks per stage-1 slab: 256 G, i.e. 32 KB of scores for the 32 / G queries of a workgroup.
+__host__ __device__ constexpr int ts_slab_blocks(int G) { return 256 * G; }
 
-// Byte offsets of the stage-2 workgroup's LDS regions. The merged block list (scores, ids) and
-// the token logits and scores share the first region: the list is consumed before any token is
-// scored.
+// Byte offsets of the token workgroup's LDS regions. The candidates' scores and, at the end, the
+// waves' partial outputs share the first region.
 struct TsTokenLayout {
-  int64_t mk, mg, zs, keys, kb, kp, qs, red, hist, total;
+  int64_t keys, red, kb, kp, zk, qs, hist, total;
 };
 __host__ __device__ inline int64_t ts_al16(int64_t x) { return (x + 15) / 16 * 16; }
-__host__ __device__ inline TsTokenLayout ts_token_layout(int d, int G, int64_t merge, int64_t C0, int64_t s1,
-                                                        int64_t s0) {
+__host__ __device__ inline TsTokenLayout ts_token_layout(int d, int G, int64_t C0, int64_t s1, int64_t s0) {
   TsTokenLayout L{};
-  L.mk = 0;
-  L.mg = ts_al16(merge * 4);
-  L.zs = 0;
-  L.keys = ts_al16(C0 * G * 4);
-  const int64_t tok = L.keys + ts_al16(C0 * 4), mrg = 2 * ts_al16(merge * 4);
-  int64_t off = tok > mrg ? tok : mrg;
+  const int64_t sc = ts_al16(C0 * 4), red = ts_al16(4 * static_cast<int64_t>(G) * d * 4);
+  int64_t off = sc > red ? sc : red;
+  L.keys = 0;
+  L.red = 0;
   L.kb = off;
   off += ts_al16(s1 * 4);
   L.kp = off;
   off += ts_al16(s0 * 4);
+  L.zk = off;
+  off += ts_al16(s0 * G * 4);
   L.qs = off;
   off += ts_al16(static_cast<int64_t>(G) * d * 4);
-  L.red = off;
-  off += ts_al16(4 * static_cast<int64_t>(G) * d * 4);
   L.hist = off;
   off += 256 * 4;
   L.total = off;
   return L;
 }
+// LDS of the merge workgroup: the merged list (scores, ids) and a histogram.
+size_t ts_merge_lds_bytes(int64_t merge);
 
 // q1[row] = round(rot(q[row], p1)), q0[row] = round(rot(q[row], p0)) for rows = B n_q H_q (copies
 // without rotation).
 hipError_t launch_ts_rotate_queries(const void* q, void* q1, void* q0, int64_t rows, int64_t p1, int64_t p0, int d,
                                     bool bf16, const InvFreq& iv, int use_rope, hipStream_t s);
 hipError_t launch_ts_score(const TsArgs& a, int d, bool bf16, int G, hipStream_t s);
+hipError_t launch_ts_merge(const TsArgs& a, hipStream_t s);
 hipError_t launch_ts_tokens(const TsArgs& a, int d, bool bf16, int G, size_t lds, int64_t B, hipStream_t s);
 
 }  // namespace recsa

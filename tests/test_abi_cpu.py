@@ -157,16 +157,17 @@ def test_error_paths_return_status_before_launch():
 
 def test_two_stage_sizes_and_error_paths():
     """Workspace = RoPE table (rows 0..C0) + queries rotated at two positions + rotated block keys
-    (unless given) + the per-slab candidate lists; bad arguments are rejected before any launch."""
+    (unless given) + the per-slab candidate lists + the kept block ids; bad arguments are rejected
+    before any launch."""
     sh = _shape(batch=4, capacity=1 << 19)
     n, nq, kb, kt = 1 << 19, 256, 128, 512
     n1 = n // 16
     C0 = 16 * kb
-    SB = 1920                                   # blocks per slab for 4 query heads per KV head, bf16
+    SB = 1024                                   # blocks per slab for 4 query heads per KV head
     slabs = -(-n1 // SB)
     al = lambda x: (x + 255) // 256 * 256
     want = (al((C0 + 1) * 64 * 8) + 2 * al(4 * nq * 32 * 128 * 2) + al(4 * 8 * n1 * 128 * 2)
-            + al(4 * 8 * nq * slabs * kb * 8))
+            + al(4 * 8 * nq * slabs * kb * 8) + al(4 * 8 * nq * kb * 4))
     assert R.recsa_two_stage_workspace_bytes(sh, n, nq, kb, kt) == want
     assert R.recsa_two_stage_workspace_bytes(sh, n, nq, kb, kt, blocks_rotated=True) == want - al(4 * 8 * n1 * 128 * 2)
     t = _FakeTensor()

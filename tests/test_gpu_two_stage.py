@@ -86,7 +86,7 @@ def _compare(w, res, ref, min_match=0.9):
 
 # (workload, k_block, k_token)
 CASES = [
-    # 4000 blocks: three stage-1 slabs (1920, 1920, 160), merged
+    # 4000 blocks: four stage-1 slabs (1024, 1024, 1024, 928), merged
     (_w("ts_bf16_d128_G4_f16_slabs", Hq=8, Hkv=2, d=128, dtype="bf16", L=16 * 4000 + 5, n_queries=5, seed=81), 16, 100),
     (_w("ts_f32_d64_G2_f4", B=2, Hq=4, Hkv=2, d=64, dtype="f32", L=3001, f=4, n_queries=4, seed=82), 6, 13),
     (_w("ts_bf16_d128_G8_f32_keep_tokens", Hq=8, Hkv=1, d=128, dtype="bf16", L=32 * 300 + 31, f=32, n_queries=3,
@@ -121,6 +121,28 @@ def test_two_stage_edge_cases():
         _say(f"two-stage edges: n={n} k_block={kb} k_token={kt}")
         res = _run(g, n, kb, kt)
         ref = two_stage_decode(inp["K"], inp["V"], inp["W"], inp["q"], n, w.f, kb, kt, w.dtype, w.theta)
+        _compare(w, res, ref, min_match=1.0)
+
+
+def test_two_stage_exact_ties():
+    """Exact ties everywhere (no rotation; every third block's tokens share one key, the rest are
+    zero): block scores and token logits take two values, so each selection keeps the lowest
+    indices among equal scores -- through the selections' all-equal path and their fallback for a
+    bin too full to rank -- exactly as the oracle's (score, index) order does."""
+    w = _w("ts_ties", Hq=8, Hkv=2, d=64, dtype="bf16", L=16 * 3000 + 5, n_queries=3, theta=0.0, seed=89)
+    inp = gen_decode_inputs(w)
+    rng = np.random.default_rng(7)
+    c = (rng.standard_normal(w.d) * 0.3).astype(np.float32)
+    cb = (c.view(np.uint32) >> 16).astype(np.uint16)      # bf16 bits (truncation: any bf16 value will do)
+    K = np.zeros_like(inp["K"])
+    for g0 in range(0, 3000, 3):
+        K[:, :, 16 * g0:16 * (g0 + 1)] = cb
+    inp["K"] = K
+    g = Gpu(w, inp)
+    for kb, kt in [(100, 700), (120, 1900), (7, 50)]:
+        _say(f"two-stage ties: k_block={kb} k_token={kt}")
+        res = _run(g, w.L, kb, kt)
+        ref = two_stage_decode(inp["K"], inp["V"], inp["W"], inp["q"], w.L, w.f, kb, kt, w.dtype, w.theta)
         _compare(w, res, ref, min_match=1.0)
 
 
