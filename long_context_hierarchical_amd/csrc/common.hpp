@@ -108,15 +108,6 @@ __device__ __forceinline__ void store1(void* base, int64_t off, float x) {
   }
 }
 
-// RoPE cos/sin at integer position p for inverse frequency w: the exact float64 product, float64
-// cos and sin, each rounded once to float32.
-__device__ __forceinline__ void rope_cs(int64_t p, float w, float& c, float& s) {
-  double sd, cd;
-  sincos(static_cast<double>(p) * static_cast<double>(w), &sd, &cd);
-  c = static_cast<float>(cd);
-  s = static_cast<float>(sd);
-}
-
 // Monotone map float32 -> uint32 (larger float -> larger key); -0 and +0 map alike.
 __device__ __forceinline__ uint32_t ordered_bits(float s) {
   uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);

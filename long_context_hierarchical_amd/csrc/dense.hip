@@ -17,6 +17,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "rope.hpp"
 #include "internal.hpp"
 
 namespace recsa {

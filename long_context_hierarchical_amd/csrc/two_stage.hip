@@ -30,6 +30,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "rope.hpp"
 #include "internal.hpp"
 #include "lanes.hpp"
 
