@@ -81,14 +81,15 @@ def kernel_hash(*names):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str, src_hash: str):
-    """HBM bytes per launch measured with rocprofv3 counters for this exact kernel source, if recorded."""
+def traffic_from_profiles(kernel: str, src_hash: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters for this exact kernel source on this
+    workload (the record names it, e.g. 'recsa-c2: ...'), if recorded."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("source_hash") != src_hash:
+    if rec.get("source_hash") != src_hash or not str(rec.get("workload", "")).startswith(f"recsa-{workload}:"):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -474,7 +475,7 @@ def main():
         ki = kinfo[name]
         ach = ki["bytes"] / (ki["ms"] * 1e-3) / 1e9
         r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(name, ki["src"]),
+             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(name, ki["src"], w.name),
              "kernel": name}
         if probe and "read_GBps" in probe:
             r["measured_read_peak"] = probe["read_GBps"]

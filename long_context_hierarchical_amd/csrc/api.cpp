@@ -36,6 +36,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t kMaxList = 4096;     // kept-node / candidate list capacity in LDS
 constexpr size_t kMaxLds = 65536;
+constexpr size_t kMaxLdsMerge = 163840;   // gfx950: 160 KB of LDS per workgroup
 constexpr int64_t kTableAlign = 256;
 
 struct Info {
@@ -787,12 +788,14 @@ static int32_t ts_plan(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q
   for (int64_t t = 0; t < p->n_slabs; ++t) p->merge += std::min<int64_t>(p->s1, std::min<int64_t>(p->SB, p->n1 - t * p->SB));
   const recsa::TsTokenLayout L = recsa::ts_token_layout(static_cast<int>(I.d), static_cast<int>(I.G), p->C0, p->s1,
                                                         p->s0);
-  p->lds = std::max(static_cast<size_t>(L.total), recsa::ts_merge_lds_bytes(p->merge));
+  p->lds = static_cast<size_t>(L.total);
   if (p->lds > kMaxLds)
     return fail(RECSA_ERR_UNSUPPORTED,
-                "k_block = %d and k_token = %d need %zu bytes of LDS per query (max %zu): %lld token candidates, "
-                "%lld merged blocks",
-                k_block, k_token, p->lds, kMaxLds, (long long)p->C0, (long long)p->merge);
+                "k_block = %d and k_token = %d need %zu bytes of LDS per query (max %zu): %lld token candidates",
+                k_block, k_token, p->lds, kMaxLds, (long long)p->C0);
+  if (recsa::ts_merge_lds_bytes(p->merge) > kMaxLdsMerge)
+    return fail(RECSA_ERR_UNSUPPORTED, "%lld merged block candidates per query need %zu bytes of LDS (max %zu)",
+                (long long)p->merge, recsa::ts_merge_lds_bytes(p->merge), kMaxLdsMerge);
   p->tab_bytes = p->C0 > 0 ? table_bytes(I, p->C0) : 0;
   p->q_bytes = al256(I.B * n_q * I.Hq * I.d * I.esz);
   p->kb_bytes = own_blocks && p->s1 > 0 ? al256(I.B * I.Hkv * p->n1 * I.d * I.esz) : 0;

@@ -692,8 +692,14 @@ size_t ts_merge_lds_bytes(int64_t merge) { return static_cast<size_t>(2 * ts_al1
 
 hipError_t launch_ts_merge(const TsArgs& a, hipStream_t s) {
   if (a.n_q <= 0 || a.s1 <= 0) return hipSuccess;
+  const size_t lds = ts_merge_lds_bytes(a.merge);
+  if (lds > 65536) {  // long lists (many slabs): up to gfx950's 160 KB of LDS per workgroup
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ts_merge_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid(static_cast<unsigned>(a.n_q), static_cast<unsigned>(a.BH));
-  hipLaunchKernelGGL(ts_merge_kernel, grid, dim3(256), ts_merge_lds_bytes(a.merge), s, a);
+  hipLaunchKernelGGL(ts_merge_kernel, grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
