@@ -368,7 +368,31 @@ def cpu_baseline(w, k, n_units):
                    f"{w.B * w.n_queries * w.Hkv} units (median {t_unit * 1e3:.2f} ms each); one step "
                    f"extrapolated over {P} cores: {step_s:.2f} s (sample wall {wall:.1f} s incl. input generation)"),
         "build_GBps": build_bytes(w)[0] / (w.B * w.Hkv) / t_build * P / 1e9,
+        "host": host_cpu(),
     }
+
+
+def host_cpu():
+    """The host CPU's model name and its physical core count (from /proc/cpuinfo)."""
+    model, cores = None, set()
+    try:
+        phys = core = None
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model is None:
+                    model = val
+                elif key == "physical id":
+                    phys = val
+                elif key == "core id":
+                    core = val
+                elif not key and phys is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+    except OSError:
+        pass
+    return {"model": model, "physical_cores": len(cores) or None, "usable_cpus": len(os.sched_getaffinity(0))}
 
 
 def main():
