@@ -470,13 +470,16 @@ __global__ __launch_bounds__(256) void ts_merge_kernel(TsArgs a) {
 
 // One candidate row's logits: the row (token `row`, 16 lanes, PPL rotation pairs per lane) is
 // rotated at its candidate index ic from the RoPE table and rounded to the storage type, then
-// dotted with the lane's slice of the rotated query; z_h = fp32(scale * dot). Scoring and the
-// kept rows' second pass both call this, so they produce the same bits.
+// dotted with the lane's slice of the rotated query; z_h = fp32(scale * dot). bf16 rounds and
+// packs element pairs with one conversion each and takes the dot products with v_dot2 (the
+// rotated query is exact in bf16). Scoring and the kept rows' second pass both call this, so
+// they produce the same bits.
 template <int D, bool BF16, int G>
 __device__ __forceinline__ void ts_row_logits(float (&lo)[D / 32], float (&hi)[D / 32], const float2* tab, int ic,
                                               int use_rope, int sub, const float (&qlo)[G][D / 32],
                                               const float (&qhi)[G][D / 32], float scale, float (&z)[G]) {
   constexpr int PPL = D / 32;
+  float olo[PPL], ohi[PPL];
   if (use_rope) {
     // (cos, sin) pairs PPL sub .. PPL sub + PPL - 1 of position ic, two pairs per load
     const float4* t4 = reinterpret_cast<const float4*>(tab + static_cast<int64_t>(ic) * (D / 2) + PPL * sub);
@@ -488,20 +491,46 @@ __device__ __forceinline__ void ts_row_logits(float (&lo)[D / 32], float (&hi)[D
       for (int e = 0; e < 2; ++e) {
         const int p = 2 * p2 + e;
         const float a1 = lo[p] * c2[e], a2 = hi[p] * s2[e], a3 = hi[p] * c2[e], a4 = lo[p] * s2[e];
-        lo[p] = round_store<BF16>(a1 - a2);
-        hi[p] = round_store<BF16>(a3 + a4);
+        olo[p] = a1 - a2;
+        ohi[p] = a3 + a4;
       }
     }
-  }
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    float dot = 0.0f;
+  } else {
 #pragma unroll
     for (int p = 0; p < PPL; ++p) {
-      dot = fmaf(qlo[hh][p], lo[p], dot);
-      dot = fmaf(qhi[hh][p], hi[p], dot);
+      olo[p] = lo[p];
+      ohi[p] = hi[p];
     }
-    z[hh] = lane_group_sum<16>(dot) * scale;
+  }
+  if constexpr (BF16) {
+    bf16x2_t kp[PPL];
+#pragma unroll
+    for (int u = 0; u < PPL / 2; ++u) {
+      kp[u] = pack_bf16_rne(olo[2 * u], olo[2 * u + 1]);
+      kp[PPL / 2 + u] = pack_bf16_rne(ohi[2 * u], ohi[2 * u + 1]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int u = 0; u < PPL / 2; ++u) {
+        dot = __builtin_amdgcn_fdot2_f32_bf16(kp[u], pack_bf16_rne(qlo[hh][2 * u], qlo[hh][2 * u + 1]), dot, false);
+        dot = __builtin_amdgcn_fdot2_f32_bf16(kp[PPL / 2 + u], pack_bf16_rne(qhi[hh][2 * u], qhi[hh][2 * u + 1]), dot,
+                                              false);
+      }
+      z[hh] = lane_group_sum<16>(dot) * scale;
+    }
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) {
+        dot = fmaf(qlo[hh][p], olo[p], dot);
+        dot = fmaf(qhi[hh][p], ohi[p], dot);
+      }
+      z[hh] = lane_group_sum<16>(dot) * scale;
+    }
   }
 }
 
