@@ -785,6 +785,9 @@ static int32_t ts_plan(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q
   p->s0 = std::min<int64_t>(k_token, p->C0);
   p->SB = recsa::ts_slab_blocks(static_cast<int>(I.G));
   p->n_slabs = (p->n1 + p->SB - 1) / p->SB;
+  // stage 1 launches one workgroup per (slice, slab, group of 32 / G queries), in one grid dimension
+  if (I.B * I.Hkv * p->n_slabs * ((n_q + 32 / I.G - 1) / (32 / I.G)) + 7 > INT32_MAX)
+    return fail(RECSA_ERR_UNSUPPORTED, "too many (query group, block slab) pairs for one launch");
   for (int64_t t = 0; t < p->n_slabs; ++t) p->merge += std::min<int64_t>(p->s1, std::min<int64_t>(p->SB, p->n1 - t * p->SB));
   const recsa::TsTokenLayout L = recsa::ts_token_layout(static_cast<int>(I.d), static_cast<int>(I.G), p->C0, p->s1,
                                                         p->s0);

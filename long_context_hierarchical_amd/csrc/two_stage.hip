@@ -29,6 +29,8 @@
 // "score descending, index ascending" restricted to the kept set.
 #include <math.h>
 
+#include <atomic>
+
 #include "common.hpp"
 #include "rope.hpp"
 #include "internal.hpp"
@@ -722,10 +724,16 @@ size_t ts_merge_lds_bytes(int64_t merge) { return static_cast<size_t>(2 * ts_al1
 hipError_t launch_ts_merge(const TsArgs& a, hipStream_t s) {
   if (a.n_q <= 0 || a.s1 <= 0) return hipSuccess;
   const size_t lds = ts_merge_lds_bytes(a.merge);
-  if (lds > 65536) {  // long lists (many slabs): up to gfx950's 160 KB of LDS per workgroup
+  // long lists (many slabs) use up to gfx950's 160 KB of LDS per workgroup; the kernel's limit is
+  // raised once per process to the largest size asked for so far
+  static std::atomic<size_t> allowed{65536};
+  if (lds > allowed.load()) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ts_merge_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
+    size_t cur = allowed.load();
+    while (lds > cur && !allowed.compare_exchange_weak(cur, lds)) {
+    }
   }
   const dim3 grid(static_cast<unsigned>(a.n_q), static_cast<unsigned>(a.BH));
   hipLaunchKernelGGL(ts_merge_kernel, grid, dim3(256), lds, s, a);
