@@ -359,20 +359,38 @@ __global__ __launch_bounds__(256) void dense_mfma16_kernel(DenseArgs a) {
   for (int t = 0; t < DT; ++t) o[t] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
   float m_run = -INFINITY, l_run = 0.0f;
 
+  // K/V tiles are double-buffered in registers: the next tile's rows are requested before this
+  // tile is multiplied. Every key row is read by one workgroup only (one query per sequence), so
+  // the loads carry the non-temporal hint.
+  constexpr int LPT = KT * (D / 8) / 256;   // 16-byte pieces per thread per tile, for K and for V
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  u32x4v kn[LPT], vn[LPT];
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int c = tid + 256 * u;
+      const int r = c / (D / 8), ch = c % (D / 8);
+      const int64_t key = k0 + r < k_hi ? k0 + r : k_hi - 1;   // rows past the range: zeroed when stored
+      kn[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(
+          static_cast<const uint16_t*>(a.Kr) + (bh * a.kr_rows + key) * D + ch * 8));
+      vn[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(
+          static_cast<const uint16_t*>(a.V) + (bh * a.v_rows + key) * D + ch * 8));
+    }
+  };
+  if (k_lo < k_hi) fetch(k_lo);
   for (int64_t k0 = k_lo; k0 < k_hi; k0 += KT) {
     __syncthreads();
-    for (int c = tid; c < KT * (D / 8); c += 256) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int c = tid + 256 * u;
       const int r = c / (D / 8), ch = c % (D / 8);
-      const int64_t key = k0 + r;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (key < k_hi) {
-        kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Kr) + (bh * a.kr_rows + key) * D + ch * 8);
-        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.V) + (bh * a.v_rows + key) * D + ch * 8);
-      }
-      *reinterpret_cast<uint4*>(&Ks[r * KPAD + ch * 8]) = kv;
-      *reinterpret_cast<uint4*>(&Vs[r * VPAD + ch * 8]) = vv;
+      const bool ok = k0 + r < k_hi;
+      const u32x4v z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4v*>(&Ks[r * KPAD + ch * 8]) = ok ? kn[u] : z;
+      *reinterpret_cast<u32x4v*>(&Vs[r * VPAD + ch * 8]) = ok ? vn[u] : z;
     }
     __syncthreads();
+    if (k0 + KT < k_hi) fetch(k0 + KT);
 
     // S^T: 4 sub-tiles of 16 keys x 16 rows; lane holds keys 16*s4 + 4*g4 + i of row r16
     f32x4_t st[4];
