@@ -9,7 +9,7 @@ One step = the whole hot path on that batch: build the tree over all 4 x 524,288
 level-index RoPE, per-level top-k, one softmax) in one call. Inputs are resident in HBM
 before timing starts. `value` is decode queries per second of whole-step time.
 
-Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+Prints one JSON line. --gpus above 1 is refused: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
@@ -398,7 +398,7 @@ def host_cpu():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the path shards by (sequence, KV head) with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)

@@ -1,7 +1,6 @@
 """Two-stage block-then-token selection over the RecSA cache -- plain CPU oracle.
 
-TEST INFRASTRUCTURE ONLY. Imported by tests/ and the benchmark's CPU-baseline leg; never by
-the product path.
+TEST INFRASTRUCTURE ONLY. Imported by tests/; never by the product path.
 
 Sources, cited by page title and section:
   [HISA]      "HISA: Efficient Hierarchical Indexing for Fine-Grained Sparse Attention" --
