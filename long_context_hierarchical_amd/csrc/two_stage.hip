@@ -725,14 +725,24 @@ hipError_t launch_ts_merge(const TsArgs& a, hipStream_t s) {
   if (a.n_q <= 0 || a.s1 <= 0) return hipSuccess;
   const size_t lds = ts_merge_lds_bytes(a.merge);
   // long lists (many slabs) use up to gfx950's 160 KB of LDS per workgroup; the kernel's limit is
-  // raised once per process to the largest size asked for so far
-  static std::atomic<size_t> allowed{65536};
-  if (lds > allowed.load()) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ts_merge_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  // raised on each device (the attribute belongs to the current device) to the largest size asked
+  // for so far there
+  constexpr int kDevices = 64;
+  static std::atomic<size_t> allowed[kDevices];   // 0: never raised (64 KB)
+  if (lds > 65536) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    size_t cur = allowed.load();
-    while (lds > cur && !allowed.compare_exchange_weak(cur, lds)) {
+    std::atomic<size_t>* lim = dev >= 0 && dev < kDevices ? &allowed[dev] : nullptr;
+    if (lim == nullptr || lds > lim->load()) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ts_merge_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+      if (lim != nullptr) {
+        size_t cur = lim->load();
+        while (lds > cur && !lim->compare_exchange_weak(cur, lds)) {
+        }
+      }
     }
   }
   const dim3 grid(static_cast<unsigned>(a.n_q), static_cast<unsigned>(a.BH));
