@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
 
   // rotated query operands for the current level -> qr: lane slot ssub holds the 8
   // rotate-half pairs (elements 8*ssub + e and HALF + 8*ssub + e, e < 8) of every head
-  auto rotate_query = [&](int64_t pos) {
+  auto rotate_query = [&](int64_t pos) __attribute__((always_inline)) {
     float c[8], s[8];
     if (a.use_rope) {
       const float4* t = reinterpret_cast<const float4*>(a.tab + pos * HALF + 8 * ssub);
