@@ -240,8 +240,8 @@ struct RawV {
 };
 
 // NW waves per unit. NW = 1: one wave does everything. NW > 1 (few units, latency-bound):
-// the waves share the score passes, wave 0 alone selects and computes the softmax weights,
-// and each wave owns D / NW of the value dimensions with the same row-group accumulation
+// the waves share the score passes, wave 0 alone selects, wave h mod NW computes query head
+// h's softmax weights, and each wave owns D / NW of the value dimensions with the same row-group accumulation
 // chains as one wave, so every output element is accumulated in exactly the same order and
 // the results are bitwise those of NW = 1. When the launcher grants the LDS (pv_stage), the
 // value rows of a softmax chunk are staged through LDS by all threads with 16-byte loads
@@ -644,11 +644,41 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
       st3 = piece(s0, 3);
     };
     if constexpr (NW > 1) {
-      if (staged) stage_issue(0);   // in flight during wave 0's weight pass
+      if (staged) stage_issue(0);   // in flight during the weight pass
       // this wave's prefetched rows have landed in LDS before the barrier below
       if (prefetched) __builtin_amdgcn_s_waitcnt(0);
     }
-    if (wid == 0) {
+    if constexpr (NW > 1) {
+      // several waves: head hh's weights are computed by wave hh % NW, in the order one wave
+      // uses for it (each head's max, exponentials and sum are independent of the other heads),
+      // and its running max lives in that wave; every wave takes alpha and the running sum
+      // from LDS
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        if (hh % NW != wid) continue;
+        float mn = -INFINITY;
+        for (int32_t r = lane; r < cn; r += kWave) {
+          if (use_flags && flags[r]) continue;
+          mn = fmaxf(mn, zs[r * G + hh]);
+        }
+        mn = fmaxf(m_run[hh], wave_max_dpp(mn));
+        float ls = 0.0f;
+        for (int32_t r = lane; r < cn; r += kWave) {
+          const bool skip = use_flags && flags[r];
+          const float p = skip ? 0.0f : expf(zs[r * G + hh] - mn);
+          zs[r * G + hh] = p;
+          ls += p;
+        }
+        const float lsum = wave_sum_dpp(ls);
+        const float alpha = expf(m_run[hh] - mn);
+        const float lnew = l_run[hh] * alpha + lsum;
+        m_run[hh] = mn;
+        if (lane == 0) {
+          bc[hh] = alpha;
+          bc[G + hh] = lnew;
+        }
+      }
+    } else {
       float mnew[G];
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) mnew[hh] = -INFINITY;
@@ -684,24 +714,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
         m_run[hh] = mnew[hh];
 #pragma unroll
         for (int e = 0; e < VEW; ++e) acc[hh][e] *= alpha;
-        if constexpr (NW > 1) {
-          if (lane == 0) {
-            bc[hh] = alpha;
-            bc[G + hh] = l_run[hh];
-          }
-        }
       }
     }
     bsync();
     if constexpr (NW > 1) {
-      if (wid != 0) {
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float alpha = bc[hh];
-          l_run[hh] = bc[G + hh];
+      for (int hh = 0; hh < G; ++hh) {
+        const float alpha = bc[hh];
+        l_run[hh] = bc[G + hh];
 #pragma unroll
-          for (int e = 0; e < VEW; ++e) acc[hh][e] *= alpha;
-        }
+        for (int e = 0; e < VEW; ++e) acc[hh][e] *= alpha;
       }
       // 8 rows of the residue per step from LDS rows [0, sn) of vst (rows up to the next
       // multiple of 8 * RPP hold finite copies), their reads issued together and no branch: a
@@ -866,10 +888,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
       }
     }
   }
-  if (a.lse && wid == 0) {
+  if (a.lse) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      if (lane == hh) {
+      // the wave that holds head hh's running max (wave 0 alone with one wave)
+      if (hh % NW == wid && lane == 0) {
         a.lse[(b * a.n_q + j) * a.Hq + static_cast<int64_t>(h) * G + hh] =
             l_run[hh] > 0.0f ? m_run[hh] + logf(l_run[hh]) : -INFINITY;
       }
