@@ -563,15 +563,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     if (a.use_rope) score_rows_t(src, vsrc, rowbase, cm, c0, cn, qpos, std::true_type{});
     else score_rows_t(src, vsrc, rowbase, cm, c0, cn, qpos, std::false_type{});
   };
-  // Keeps the s largest (S, -r) keys among r < C: flags[r] = 1 and sel_out[0..s) = their
-  // node ids in candidate order. A threshold is found by bisection on the scores'
-  // order-preserving 32-bit patterns (a ballot count per step, no lane exchange); the
-  // candidates above it are kept, then those equal to it in index order.
-  auto select_top = [&](int32_t C, int32_t s, int32_t* sel_out) {
+  // NU: candidate slots per lane held in registers (C <= NU * 64 unless GEN); GEN: the slots
+  // past NU are read from LDS. Slots past the last candidate hold key 0, which no threshold
+  // t > 0 counts, so the result does not depend on NU.
+  auto select_top_n = [&](int32_t C, int32_t s, int32_t* sel_out, auto nu_t, auto gen_t) {
+    constexpr int NU = decltype(nu_t)::value;
+    constexpr bool GEN = decltype(gen_t)::value;
     const int32_t nu = (C + kWave - 1) / kWave;
-    uint32_t o[4];
+    uint32_t o[NU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const int32_t r = lane + kWave * u;
       o[u] = r < C ? ordered_bits(sc[r]) : 0u;
     }
@@ -583,8 +584,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     auto count_ge = [&](uint32_t t) -> int32_t {
       int32_t c = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) c += __popcll(__ballot(o[u] >= t));
-      for (int u = 4; u < nu; ++u) c += __popcll(__ballot(key(u) >= t));
+      for (int u = 0; u < NU; ++u) c += __popcll(__ballot(o[u] >= t));
+      if constexpr (GEN)
+        for (int u = NU; u < nu; ++u) c += __popcll(__ballot(key(u) >= t));
       return c;
     };
     // tau: the largest t with at least s keys >= t; once exactly s keys are >= some t they
@@ -600,8 +602,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     }
     int32_t above = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) above += __popcll(__ballot(o[u] > tau));
-    for (int u = 4; u < nu; ++u) above += __popcll(__ballot(key(u) > tau));
+    for (int u = 0; u < NU; ++u) above += __popcll(__ballot(o[u] > tau));
+    if constexpr (GEN)
+      for (int u = NU; u < nu; ++u) above += __popcll(__ballot(key(u) > tau));
     const int32_t need = s - above;   // keys equal to tau to keep, lowest index first
     const uint64_t lt = (1ull << lane) - 1ull;
     int32_t taken = 0, cnt = 0;
@@ -617,10 +620,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
       cnt += __popcll(km);
     };
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < NU; ++u)
       if (u < nu) emit(u, o[u]);
-    for (int u = 4; u < nu; ++u) emit(u, key(u));
+    if constexpr (GEN)
+      for (int u = NU; u < nu; ++u) emit(u, key(u));
     wave_sync();
+  };
+  // Keeps the s largest (S, -r) keys among r < C: flags[r] = 1 and sel_out[0..s) = their
+  // node ids in candidate order. A threshold is found by bisection on the scores'
+  // order-preserving 32-bit patterns (a ballot count per step, no lane exchange); the
+  // candidates above it are kept, then those equal to it in index order. Each step counts
+  // only the lane slots that can hold a candidate (two at f = 16, k = 8).
+  auto select_top = [&](int32_t C, int32_t s, int32_t* sel_out) {
+    if (C <= 2 * kWave) select_top_n(C, s, sel_out, std::integral_constant<int, 2>{}, std::false_type{});
+    else if (C <= 3 * kWave) select_top_n(C, s, sel_out, std::integral_constant<int, 3>{}, std::false_type{});
+    else if (C <= 4 * kWave) select_top_n(C, s, sel_out, std::integral_constant<int, 4>{}, std::false_type{});
+    else select_top_n(C, s, sel_out, std::integral_constant<int, 4>{}, std::true_type{});
   };
 
   // fold entries r < cn (skipping kept ones when use_flags) into the online softmax: wave 0
