@@ -118,6 +118,55 @@ def decode_bytes_per_query(w, k):
     return rows * w.d * w.elem_bytes * w.Hkv, dict(key_rows=key_rows, val_rows=val_rows, tok_rows=C0)
 
 
+def decode_unique_bytes(w, k, sel):
+    """Bytes of the distinct rows one decode call reads (the union over its queries, per
+    sequence and KV head), from the kernel's selections sel [B][n_q][H_kv][T][width] (kept ids
+    ascending, -1 padded): the key of every candidate of a level that is scored, the value of
+    every candidate that some query did not keep, and the key and value of every token-level
+    candidate. A level whose candidates are all kept reads nothing."""
+    import numpy as np
+    sel = np.asarray(sel)
+    B, nq, H, T = sel.shape[:4]
+    f, L = w.f, w.L
+    nl, m = [], L // f
+    while m >= 1:
+        nl.append(m)
+        m //= f
+    if len(nl) != T:
+        raise ValueError(f"sel holds {T} levels, the context has {len(nl)}")
+    slab = np.arange(B * H, dtype=np.int64).reshape(B, H, 1)
+
+    def per_slice(ids, n):
+        # ids [B][n_q][H][c] -> flat indices into a [B * H * n] count array
+        flat = ids.transpose(0, 2, 1, 3).reshape(B, H, -1).astype(np.int64)
+        return (slab * n + flat).ravel()
+
+    rows, s_up, n_up, parents = 0, 0, 0, None
+    for lv in range(T, 0, -1):
+        n_l = nl[lv - 1]
+        C = f * s_up + (n_l - f * n_up)
+        s = min(int(k[lv - 1]), C)
+        kept = sel[:, :, :, lv - 1, :s]
+        if s < C:
+            cand = np.zeros(B * H * n_l, np.int64)
+            if s_up:
+                kids = parents[..., None].astype(np.int64) * f + np.arange(f)
+                cand += np.bincount(per_slice(kids.reshape(B, nq, H, -1), n_l), minlength=B * H * n_l)
+            cand = cand.reshape(B, H, n_l)
+            cand[:, :, f * n_up:] += nq
+            ksel = np.bincount(per_slice(kept, n_l), minlength=B * H * n_l).reshape(B, H, n_l)
+            rows += int((cand > 0).sum()) + int((cand > ksel).sum())
+        parents, s_up, n_up = kept, s, n_l
+    tok = np.zeros(B * H * L, bool)
+    if s_up:
+        kids = parents[..., None].astype(np.int64) * f + np.arange(f)
+        tok[per_slice(kids.reshape(B, nq, H, -1), L)] = True
+    tok = tok.reshape(B, H, L)
+    tok[:, :, f * n_up:] = True
+    rows += 2 * int(tok.sum())
+    return rows * w.d * w.elem_bytes
+
+
 def build_bytes(w):
     """Read every token row of K and V once, write every node key and value once (all levels)."""
     nodes, m = 0, w.L // w.f
@@ -491,7 +540,8 @@ def main():
     kinfo = {
         "pool_kernel": dict(bytes=bb / build_launches, ms=build_ms / build_launches,
                             src=kernel_hash("build_tree.hip", "common.hpp")),
-        "attend_kernel": dict(bytes=db, ms=decode_ms, src=kernel_hash("attend.hip", "common.hpp", "lanes.hpp")),
+        "attend_kernel": dict(bytes=db, ms=decode_ms, src=kernel_hash("attend.hip", "common.hpp", "lanes.hpp"),
+                              unique=decode_unique_bytes(w, k, sel.cpu().numpy())),
     }
     dom = "pool_kernel" if build_ms >= decode_ms else "attend_kernel"
 
@@ -504,6 +554,13 @@ def main():
         if probe and "read_GBps" in probe:
             r["measured_read_peak"] = probe["read_GBps"]
             r["frac_of_measured_read"] = round(ach / probe["read_GBps"], 4)
+        if "unique" in ki:
+            # the distinct rows of the call (union over its queries, from its own selections):
+            # what it must at least bring from HBM, as against the per-query row bytes above
+            ua = ki["unique"] / (ki["ms"] * 1e-3) / 1e9
+            r["unique_bytes"] = ki["unique"]
+            r["achieved_unique"] = round(ua, 1)
+            r["frac_unique"] = round(ua / HBM_PEAK_GBS, 4)
         if name == "pool_kernel" and probe and "read16_write1_GBps" in probe:
             # the build reads every child row once and writes one node row per f rows read
             r["measured_mix_peak"] = probe["read16_write1_GBps"]
