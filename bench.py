@@ -286,15 +286,159 @@ def sweep():
                       "decode": decode_rows, "prefill_chunked_4096": prefill_rows}), flush=True)
 
 
-def decode_alu(w, rows, n_queries, decode_ms):
-    """The decode kernel against the vector-ALU roofline (it is issue-bound, its row reads
-    mostly hit the cache): algorithmic flops 2 * d * H_q * (scored rows + softmax entries) per
-    query, i.e. one multiply-add per (query head, element) for every logit and every weighted
-    value row; key rotation, selection and exponentials are not counted."""
-    per_query = 2 * w.d * w.Hq * (rows["key_rows"] + rows["tok_rows"] + rows["val_rows"] + rows["tok_rows"])
-    ach = per_query * n_queries / (decode_ms * 1e-3) / 1e12
-    return {"bound": "alu", "achieved": round(ach, 2), "peak": 157.3, "unit": "TFLOP/s",
-            "frac": round(ach / 157.3, 4), "flops_per_query": per_query}
+# Vector-ALU issue peak of the MI355X: 256 CUs x 4 SIMDs x 2.4 GHz, a wave64 instruction every 4
+# clocks per SIMD: 39.3 T lane-instructions/s. A v_dot2_f32_bf16 lane-instruction is 2
+# multiply-adds (the 157.3 TFLOP/s vector peak), a v_fma_f32 one (78.6 TFLOP/s).
+VALU_LANE_OPS = 256 * 4 * 2.4e9 * 64 / 4
+
+
+def shared_level(n, f, k):
+    """(level, node count) of the first level a query over n tokens scores: every level above it
+    keeps all its nodes, so its candidates are all its nodes (closed form); (0, 0) if none."""
+    nl, m = [], n // f
+    while m >= 1:
+        nl.append(m)
+        m //= f
+    for lv in range(len(nl), 0, -1):
+        if k[lv - 1] < nl[lv - 1]:
+            return lv, nl[lv - 1]
+    return 0, 0
+
+
+def valu_roofline(w, rows, n_queries, ms, mf_rows=0):
+    """The attention kernel against the vector-ALU roofline (it is issue-bound; its row reads
+    mostly hit the cache). Algorithmic work per query: one multiply-add per (query head, element)
+    for every logit computed on the vector units (the scored rows, less the first scored level's
+    mf_rows, whose logits come from the matrix cores) and for every weighted value row; key
+    rotation, selection and exponentials are not counted. Logits run on v_dot2_f32_bf16 (2
+    multiply-adds per lane-instruction; v_fma_f32 for float32 storage), values on v_fma_f32 (1):
+    the time at peak issue is logit_macs / (2 or 1) + value_macs lane-instructions over
+    VALU_LANE_OPS, and `peak` is the flop rate that time implies for this mix."""
+    logit_macs = w.d * w.Hq * (rows["key_rows"] + rows["tok_rows"] - mf_rows)
+    value_macs = w.d * w.Hq * (rows["val_rows"] + rows["tok_rows"])
+    per_dot = 2 if w.dtype == "bf16" else 1
+    t_peak = (logit_macs / per_dot + value_macs) / VALU_LANE_OPS * n_queries
+    flops = 2 * (logit_macs + value_macs) * n_queries
+    ach = flops / (ms * 1e-3) / 1e12
+    peak = flops / t_peak / 1e12
+    return {"bound": "alu", "achieved": round(ach, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+            "frac": round(t_peak / (ms * 1e-3), 4), "flops_per_query": 2 * (logit_macs + value_macs),
+            "peak_derivation": "256 CU x 4 SIMD x 2.4 GHz / 4 clk x 64 lanes; dot2 = 2 MAC, fma = 1 MAC"}
+
+
+def mfma_share(w, n_queries, ms, c_shared):
+    """The first scored level's logits on the matrix cores: 2 * d * H_q * C flops per query
+    (useful; rows past the workgroup's queries are not counted), as a rate over the whole call
+    and as a fraction of the 2.5 PFLOP/s bf16 peak."""
+    fl = 2.0 * w.d * w.Hq * c_shared * n_queries
+    ach = fl / (ms * 1e-3) / 1e12
+    return {"flops_per_call": fl, "candidates": c_shared, "achieved_over_call": round(ach, 2), "unit": "TFLOP/s",
+            "frac_of_peak_over_call": round(ach / 2500.0, 5)}
+
+
+def needle_recall(w, sel, cpu):
+    """Fraction of planted needles that end as exact token entries of their target query (the
+    needle's level-1 block kept, or the needle in the trailing partial block): over every needle
+    from the GPU call's selections sel [B][n_q][H_kv][T][width], and on the oracle's sample (the
+    CPU baseline decodes each sampled slice's needle targets) from both sides."""
+    from synthetic import needle_plan
+    if not w.needles:
+        return None
+    f, n1 = w.f, w.L // w.f
+
+    def gpu_hit(b, h, pos, tq):
+        return pos >= f * n1 or pos // f in set(int(x) for x in sel[b, tq, h, 0] if x >= 0)
+    tot = hit = 0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            for pos, tq, _hg in needle_plan(w, w.n_queries):
+                tot += 1
+                hit += gpu_hit(b, h, pos, tq)
+    out = {"gpu_all": round(hit / tot, 4), "needles": tot}
+    hits = (cpu or {}).get("_needle_hits") or []
+    if hits:
+        out["oracle_sample"] = round(sum(x[4] for x in hits) / len(hits), 4)
+        out["gpu_same_sample"] = round(sum(gpu_hit(b, h, pos, tq) for (b, h, pos, tq, _o) in hits) / len(hits), 4)
+        out["sample_needles"] = len(hits)
+        out["sample_agree"] = all(gpu_hit(b, h, pos, tq) == o for (b, h, pos, tq, o) in hits)
+    return out
+
+
+def prefill_counts(L, f, k):
+    """Closed-form (scored rows, softmax entries) summed over every causal position t < L: the
+    query at t descends over the prefix n = t + 1, its own token included; a level is scored
+    unless it keeps all its candidates."""
+    scored = entries = 0
+    for n in range(1, L + 1):
+        nl, m = [], n // f
+        while m >= 1:
+            nl.append(m)
+            m //= f
+        s_up, n_up = 0, 0
+        for lv in range(len(nl), 0, -1):
+            C = f * s_up + (nl[lv - 1] - f * n_up)
+            s = min(k[lv - 1], C)
+            if s < C:
+                scored += C
+                entries += C - s
+            s_up, n_up = s, nl[lv - 1]
+        C0 = f * s_up + (n - f * n_up) if nl else n
+        scored += C0
+        entries += C0
+    return scored, entries
+
+
+def prefill_64k_leg(R, dev, timed, probe=None):
+    """The 64K chunked-prefill workload: one sequence, 8 KV heads, bf16, f = 16, k = 8, queries at
+    every position in chunks of 4096; per chunk the tree is extended over the chunk's complete
+    blocks, then the chunk's queries attend. Timed over all 16 chunks (builds included), next to
+    the dense comparator's causal prefill of the same 65,536 positions."""
+    import numpy as np
+    import torch
+    from synthetic import WORKLOADS, gen_kv_slice, gen_queries, gen_W
+    w = WORKLOADS["c3"]
+    td = torch.bfloat16
+    sh = R.Shape(w.B, w.Hkv, w.Hq, w.d, w.f, w.dtype, w.L, 0.0, w.theta)
+    q_h = gen_queries(w, 0, w.L)
+    K = torch.empty(1, w.Hkv, w.L, w.d, dtype=td, device=dev)
+    V = torch.empty_like(K)
+    for h in range(w.Hkv):
+        Kb, Vb = gen_kv_slice(w, 0, h, q_h)
+        K[0, h] = torch.from_numpy(Kb).view(td).to(dev)
+        V[0, h] = torch.from_numpy(Vb).view(td).to(dev)
+    q = torch.from_numpy(q_h[None]).view(td).to(dev)
+    W = torch.from_numpy(gen_W(w)).view(td).to(dev)
+    T = R.recsa_num_levels(w.L, w.f)
+    k = [w.k] * T
+    tree = torch.zeros(R.recsa_tree_bytes(sh), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(R.recsa_workspace_bytes(sh, w.L, k), dtype=torch.uint8, device=dev)
+    out = torch.empty(1, w.L, w.Hq, w.d, dtype=torch.float32, device=dev)
+
+    def run():
+        for c0 in range(0, w.L, w.chunk):
+            R.recsa_build_tree(sh, K, V, W, c0, c0 + w.chunk, tree)
+            R.recsa_prefill(sh, q[:, c0:c0 + w.chunk], c0, K, V, tree, k, out[:, c0:c0 + w.chunk], None, None, 0, ws)
+    ms = timed(run, 5)
+    scored, entries = prefill_counts(w.L, w.f, k)
+    mf_rows = sum(shared_level(n, w.f, k)[1] for n in range(1, w.L + 1))
+    rows = {"key_rows": scored, "tok_rows": 0, "val_rows": entries}
+    leg = {"workload": f"recsa-c3: chunked causal prefill, L={w.L}, chunk={w.chunk}, Hq={w.Hq}, Hkv={w.Hkv}, "
+                       f"d={w.d}, fanout={w.f}, k={w.k}",
+           "ms": round(ms, 4), "tokens_per_s": round(w.L / (ms * 1e-3), 1),
+           "scored_rows": scored, "entries": entries,
+           "roofline_alu": valu_roofline(w, rows, 1, ms, mf_rows=mf_rows),
+           "mfma_first_scored_level": {"flops": 2.0 * w.d * w.Hq * mf_rows,
+                                       "achieved_over_call": round(2.0 * w.d * w.Hq * mf_rows / (ms * 1e-3) / 1e12, 3),
+                                       "unit": "TFLOP/s"}}
+    mode = R.RECSA_DENSE_CAUSAL
+    dws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, w.L, mode), 16), dtype=torch.uint8, device=dev)
+    dms = timed(lambda: R.recsa_dense_ref_attn(sh, q, 0, K, V, w.L, mode, out, None, dws), 1)
+    leg["dense_ms"] = round(dms, 3)
+    leg["dense_tokens_per_s"] = round(w.L / (dms * 1e-3), 1)
+    leg["speedup_vs_dense"] = round(dms / ms, 2)
+    del K, V, q, tree, ws, out, dws
+    torch.cuda.empty_cache()
+    return leg
 
 
 def tile_sharing(sel):
@@ -367,14 +511,22 @@ def library_legs(w, Kr, V, q, qp, c, timed):
 
 def _cpu_worker(job):
     """One worker of the CPU baseline (a separate process, one thread): generate one
-    (sequence, KV head) slice, build its tree with the oracle, decode `n_units` units."""
+    (sequence, KV head) slice, build its tree with the oracle, decode `n_units` units -- the
+    slice's needle target queries first -- and note for each needle target whether its needle
+    ended as an exact token entry (its level-1 block kept, or the token in the trailing block)."""
     name, slice_idx, n_units, k = job
     from threadpoolctl import threadpool_limits
 
     import oracle
-    from synthetic import WORKLOADS, gen_kv_slice, gen_queries, gen_W
+    from synthetic import WORKLOADS, gen_kv_slice, gen_queries, gen_W, needle_plan
     w = WORKLOADS[name]
     b, h = divmod(slice_idx, w.Hkv)
+    plan = needle_plan(w) if w.needles else []
+    targets = {}
+    for pos, tq, _hg in plan:
+        targets.setdefault(tq, []).append(pos)
+    order = list(targets) + [j for j in range(w.n_queries) if j not in targets]
+    hits = []
     with threadpool_limits(limits=1):
         q = gen_queries(w, b)
         K, V = gen_kv_slice(w, b, h, q)
@@ -383,9 +535,39 @@ def _cpu_worker(job):
         tree = oracle.build_slice(Kf, Vf, Wf, w.f, w.dtype, n_new=w.L)
         t_build = time.perf_counter() - t0
         t0 = time.perf_counter()
-        for j in range(n_units):
+        for j in order[:n_units]:
             qg = oracle.from_storage(q[j, h * w.G:(h + 1) * w.G], w.dtype)
-            oracle.attend_unit(qg, Kf, Vf, tree, w.L, w.f, k, w.dtype, w.theta)
+            r = oracle.attend_unit(qg, Kf, Vf, tree, w.L, w.f, k, w.dtype, w.theta)
+            for pos in targets.get(j, []):
+                hits.append((b, h, pos, j, bool(pos >= w.f * (w.L // w.f) or pos // w.f in r.sel.get(1, []))))
+        t_unit = (time.perf_counter() - t0) / n_units
+    return t_build, t_unit, hits
+
+
+def _cpu_prefill_worker(job):
+    """One worker of the CPU prefill baseline: generate one KV head's slice of the 64K chunked
+    prefill workload, build its tree with the oracle, and prefill `n_units` positions drawn
+    uniformly (each a descent over its prefix, its own token included)."""
+    name, h, n_units, k, seed = job
+    from threadpoolctl import threadpool_limits
+
+    import numpy as np
+
+    import oracle
+    from synthetic import WORKLOADS, gen_kv_slice, gen_queries, gen_W
+    w = WORKLOADS[name]
+    pos = np.random.default_rng(seed).integers(0, w.L, n_units)
+    with threadpool_limits(limits=1):
+        q = gen_queries(w, 0, w.L)
+        K, V = gen_kv_slice(w, 0, h, q)
+        Kf, Vf, Wf = (oracle.from_storage(x, w.dtype) for x in (K, V, gen_W(w)))
+        t0 = time.perf_counter()
+        tree = oracle.build_slice(Kf, Vf, Wf, w.f, w.dtype, n_new=w.L)
+        t_build = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for p in pos:
+            qg = oracle.from_storage(q[p, h * w.G:(h + 1) * w.G], w.dtype)
+            oracle.attend_unit(qg, Kf, Vf, tree, int(p) + 1, w.f, k, w.dtype, w.theta, self_in=True)
         t_unit = (time.perf_counter() - t0) / n_units
     return t_build, t_unit
 
@@ -398,15 +580,26 @@ def cpu_baseline(w, k, n_units):
     the GPU (the workers are forked)."""
     import multiprocessing as mp
     import statistics
+    from synthetic import WORKLOADS
     P = max(1, min(16, len(os.sched_getaffinity(0)), w.B * w.Hkv))
     jobs = [(w.name, i, n_units, list(k)) for i in range(P)]
+    wp = WORKLOADS["c3"]
+    Tp, m = 0, wp.L // wp.f
+    while m >= 1:
+        Tp, m = Tp + 1, m // wp.f
+    Pp = max(1, min(P, wp.Hkv))
+    pjobs = [("c3", h, n_units, [wp.k] * Tp, 500 + h) for h in range(Pp)]
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(P) as pool:
         res = pool.map(_cpu_worker, jobs)
-    wall = time.perf_counter() - t0
+        wall = time.perf_counter() - t0
+        pres = pool.map(_cpu_prefill_worker, pjobs)
     t_build = statistics.median(r[0] for r in res)
     t_unit = statistics.median(r[1] for r in res)
     step_s = (w.B * w.Hkv * t_build + w.B * w.n_queries * w.Hkv * t_unit) / P
+    pb = statistics.median(r[0] for r in pres)
+    pu = statistics.median(r[1] for r in pres)
+    prefill_s = (wp.Hkv * pb + wp.L * wp.Hkv * pu) / Pp
     return {
         "value": w.B * w.n_queries / step_s,
         "unit": "queries/s",
@@ -417,7 +610,14 @@ def cpu_baseline(w, k, n_units):
                    f"{w.B * w.n_queries * w.Hkv} units (median {t_unit * 1e3:.2f} ms each); one step "
                    f"extrapolated over {P} cores: {step_s:.2f} s (sample wall {wall:.1f} s incl. input generation)"),
         "build_GBps": build_bytes(w)[0] / (w.B * w.Hkv) / t_build * P / 1e9,
+        "prefill_64k": {"tokens_per_s": wp.L / prefill_s, "cores": Pp,
+                        "sample": (f"{Pp} worker processes, one thread each: each built one KV head's slice of the "
+                                   f"64K chunked-prefill workload (median {pb:.2f} s) and prefilled {n_units} "
+                                   f"positions drawn uniformly (median {pu * 1e3:.2f} ms each); all "
+                                   f"{wp.L} positions x {wp.Hkv} KV heads extrapolated over {Pp} cores: "
+                                   f"{prefill_s:.1f} s")},
         "host": host_cpu(),
+        "_needle_hits": [hh for r in res for hh in r[2]],
     }
 
 
@@ -535,6 +735,7 @@ def main():
 
     bb, n_nodes = build_bytes(w)
     qb_bytes, rows = decode_bytes_per_query(w, k)
+    mf_c = shared_level(w.L, w.f, k)[1] if w.dtype == "bf16" else 0
     db = qb_bytes * n_queries
     build_launches = pool_launches(w)
     kinfo = {
@@ -555,12 +756,19 @@ def main():
             r["measured_read_peak"] = probe["read_GBps"]
             r["frac_of_measured_read"] = round(ach / probe["read_GBps"], 4)
         if "unique" in ki:
-            # the distinct rows of the call (union over its queries, from its own selections):
-            # what it must at least bring from HBM, as against the per-query row bytes above
+            # HBM counts the distinct rows of the call (the union over its queries, from its own
+            # selections): what it must at least bring from HBM. The per-query row bytes (what
+            # the queries would read with no sharing, mostly cache hits) are an effective
+            # bandwidth, reported apart.
             ua = ki["unique"] / (ki["ms"] * 1e-3) / 1e9
-            r["unique_bytes"] = ki["unique"]
-            r["achieved_unique"] = round(ua, 1)
-            r["frac_unique"] = round(ua / HBM_PEAK_GBS, 4)
+            r["effective_GBps"] = r["achieved"]
+            r["effective_frac"] = r["frac"]
+            r["per_query_row_bytes"] = ki["bytes"]
+            r["achieved"] = round(ua, 1)
+            r["frac"] = round(ua / HBM_PEAK_GBS, 4)
+            r["algorithmic_bytes"] = ki["unique"]
+            if probe and "read_GBps" in probe:
+                r["frac_of_measured_read"] = round(ua / probe["read_GBps"], 4)
         if name == "pool_kernel" and probe and "read16_write1_GBps" in probe:
             # the build reads every child row once and writes one node row per f rows read
             r["measured_mix_peak"] = probe["read16_write1_GBps"]
@@ -592,7 +800,9 @@ def main():
             "decode_bytes_per_query": qb_bytes, "decode_rows_per_unit": rows,
             "build_bytes": bb, "tree_nodes_per_slice": n_nodes,
             "roofline_other": roof("attend_kernel" if dom == "pool_kernel" else "pool_kernel"),
-            "decode_alu": decode_alu(w, rows, n_queries, decode_ms),
+            "decode_alu": valu_roofline(w, rows, n_queries, decode_ms, mf_rows=mf_c),
+            "decode_mfma_first_scored_level": mfma_share(w, n_queries, decode_ms, mf_c),
+            "needle_recall": needle_recall(w, sel.cpu().numpy(), cpu),
             "hbm_probe": probe,
         },
     }
@@ -641,9 +851,10 @@ def main():
         legs["recsa_prefill_last_chunk"] = {"ms_per_call": round(ms, 4), "tokens_per_call": w.B * c,
                                             "tokens_per_s": round(w.B * c / (ms * 1e-3), 1),
                                             "positions": [w.L - c, w.L],
-                                            # per-unit kernel on the vector ALUs; a position within c
-                                            # of L scores and reads what a query at L does
-                                            "roofline_alu": decode_alu(w, rows, w.B * c, ms)}
+                                            # a position within c of L scores and reads what a
+                                            # query at L does
+                                            "roofline_alu": valu_roofline(w, rows, w.B * c, ms, mf_rows=mf_c),
+                                            "mfma_first_scored_level": mfma_share(w, w.B * c, ms, mf_c)}
         psw = R.recsa_sel_width(sh, w.L - c + 1, w.L, k)
         psel = torch.empty(w.B, c, w.Hkv, len(k), psw, dtype=torch.int32, device=dev)
         R.recsa_prefill(sh, qp, w.L - c, K, V, tree, k, pout, None, psel, psw, pws)
@@ -840,7 +1051,14 @@ def main():
         torch.cuda.synchronize()
         res["breakdown"]["calib_copy_bytes"] = 1 << 30
 
+    if not args.no_legs:
+        log("64K chunked prefill workload")
+        res["breakdown"]["prefill_64k"] = prefill_64k_leg(R, dev, timed)
+        if cpu is not None:
+            res["breakdown"]["prefill_64k"]["cpu_oracle_tokens_per_s"] = round(cpu["prefill_64k"]["tokens_per_s"], 2)
+
     if cpu is not None:
+        cpu.pop("_needle_hits", None)
         res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 

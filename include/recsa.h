@@ -18,13 +18,13 @@
  * are the children of the nodes it kept one level up, followed by the nodes
  * that have no complete parent; it keeps the min(k_l, C_l) candidates with
  * the highest score (the scaled RoPE logit summed over the query heads that
- * share the KV head, ties to the lower candidate index) [Abstract]. Every
- * candidate's key is rotated at its index among its level's candidates and
- * the query at C_l [Abstract, Position]; at the token level the candidates are
- * the tokens under the kept level-1 nodes plus the trailing partial block,
- * and the query sits at C_0, or C_0 - 1 when its own token is a candidate.
- * The candidates not kept, each with its node's mean value, and the
- * token-level candidates share one softmax per query head [Abstract].
+ * share the KV head, ties to the lower candidate index) [Abstract]. The
+ * candidate at position i of a level's list is rotated at i, the query at C_l
+ * [Abstract, Position]; at the token level the candidates are the tokens
+ * under the kept level-1 nodes plus the trailing partial block, and the query
+ * sits at C_0, or C_0 - 1 when its own token is a candidate. Per query head a
+ * single softmax weighs the dropped candidates (with their nodes' mean values)
+ * together with the token-level candidates [Abstract].
  *
  * Conventions for every entry point:
  *   - Pointers marked [dev] are caller-owned HIP device memory; [host] are

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "librecsa.so")
-SOURCES = ["build_tree.hip", "step.hip", "attend.hip", "backward.hip", "distill.hip", "dense.hip", "two_stage.hip", "api.cpp"]
+SOURCES = ["build_tree.hip", "step.hip", "attend.hip", "backward.hip", "distill.hip", "dense.hip", "two_stage.hip",
+           "api.cpp"]
 # HBM read/copy probe (a separate program, not part of the library): the achievable bandwidth
 PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
 PROBE = os.path.join(PKG, "probe", "hbm_probe")
@@ -31,21 +32,28 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    from concurrent.futures import ThreadPoolExecutor
     cc = hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         if not os.path.exists(path):
             continue
         obj = os.path.join(objdir, src.rsplit(".", 1)[0] + ".o")
-        cmd = [cc, *COMMON, "-c", path, "-o", obj]
+        cmds.append([cc, *COMMON, "-c", path, "-o", obj])
+        objs.append(obj)
+    # the translation units are independent: compile them side by side
+    n = jobs or max(1, min(len(cmds), len(os.sched_getaffinity(0)), 16))
+
+    def run(cmd):
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        objs.append(obj)
+    with ThreadPoolExecutor(n) as ex:
+        list(ex.map(run, cmds))
     tmp = OUT + ".tmp"
     cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

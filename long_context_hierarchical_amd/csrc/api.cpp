@@ -157,6 +157,30 @@ int32_t max_kept(int64_t n, int64_t f, const int32_t* k) {
   return static_cast<int32_t>(best);
 }
 
+// The largest max_kept(n) over n_min <= n <= n_max. Level counts above the tokens depend on n
+// only through n_1 = floor(n / f), so one n per n_1 is enough, and the walk (from the top of the
+// range down) stops once it reaches the data-independent bound min(k_l, B_l) of bounds_for:
+// usually at its first step.
+int32_t max_kept_range(const Info& I, int64_t n_min, int64_t n_max, const int32_t* k) {
+  const Bounds bd = bounds_for(I, n_max, k);
+  int64_t ub = 0;
+  {
+    int64_t S_up = 0;
+    for (int lv = bd.T; lv >= 1; --lv) {
+      const int64_t Bl = std::min(nodes_at(n_max, I.f, lv), I.f * S_up + I.f - 1);
+      const int64_t Sl = std::min<int64_t>(k[lv - 1], Bl);
+      ub = std::max(ub, Sl);
+      S_up = Sl;
+    }
+  }
+  int32_t best = 0;
+  for (int64_t n1 = n_max / I.f; n1 >= n_min / I.f && n1 >= 0; --n1) {
+    best = std::max(best, max_kept(std::max(n1 * I.f, n_min), I.f, k));
+    if (best >= ub) break;
+  }
+  return best;
+}
+
 int64_t table_bytes(const Info& I, int64_t P) {
   if (I.theta == 0.0f) return 0;
   return ((P + 1) * (I.d / 2) * static_cast<int64_t>(sizeof(float2)) + kTableAlign - 1) / kTableAlign * kTableAlign;
@@ -208,8 +232,7 @@ int32_t prepare_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, c
   if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(tree) || !aligned16(out) || !aligned16(ws))
     return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
   if (sel) {
-    int32_t need = 0;
-    for (int64_t n = n_min; n <= n_max; ++n) need = std::max(need, max_kept(n, I.f, k));
+    const int32_t need = max_kept_range(I, n_min, n_max, k);
     if (sel_width < need) return fail(RECSA_ERR_INVALID_ARG, "sel_width %d < %d kept nodes", sel_width, need);
   }
   const Bounds bd = bounds_for(I, n_max, k);
@@ -321,9 +344,7 @@ int32_t recsa_sel_width(const recsa_shape_t* shape, int64_t n_min, int64_t n_max
     return -1;
   }
   if (check_k(k, n_levels, levels_of(n_max, I.f))) return -1;
-  int32_t need = 0;
-  for (int64_t n = n_min; n <= n_max; ++n) need = std::max(need, max_kept(n, I.f, k));
-  return need;
+  return max_kept_range(I, n_min, n_max, k);
 }
 
 int64_t recsa_workspace_bytes(const recsa_shape_t* shape, int64_t n_max, const int32_t* k, int32_t n_levels) {
@@ -523,8 +544,7 @@ int32_t recsa_backward(const recsa_shape_t* shape, int32_t causal, const void* q
   if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(W) || !aligned16(tree) || !aligned16(out) ||
       !aligned16(dout) || !aligned16(dq) || !aligned16(dK) || !aligned16(dV) || !aligned16(dW) || !aligned16(workspace))
     return fail(RECSA_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
-  int32_t need = 0;
-  for (int64_t n = n_min; n <= n_max; ++n) need = std::max(need, max_kept(n, I.f, k));
+  const int32_t need = max_kept_range(I, n_min, n_max, k);
   if (sel_width < std::max(need, 1)) return fail(RECSA_ERR_INVALID_ARG, "sel_width %d < %d kept nodes", sel_width, need);
   const int64_t tab = table_bytes(I, bd.P);
   const int64_t need_ws = tab + grad_level_offset(I, levels_of(I.cap, I.f) + 1, 0);

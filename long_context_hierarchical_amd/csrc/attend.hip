@@ -1,13 +1,14 @@
 // RecSA descent + one softmax: one wave (64 lanes) per (sequence, query, KV head).
 //
-// RecSA abstract ("Recursive Sparse Attention: Million-Token Length
-// Extrapolation at Logarithmic Cost"): a query keeps at most k candidates per
-// level above the tokens, so it reads O(log L) entries; every entry's RoPE
-// position is its index among its level's candidates; the summaries of the
-// candidates it does not keep share one softmax with the exact tokens.
-// Explainer page ("Recursive Sparse Attention RecSA: Million-Token Context
-// Extrapolation at Logarithmic Cost", section "Core Idea"): coarse filtering
-// at the upper levels, then level by level down to the tokens.
+// Method: "Recursive Sparse Attention: Million-Token Length Extrapolation at
+// Logarithmic Cost", abstract. Per tree level only k candidates survive, which
+// bounds the rows a query touches by a multiple of the tree height; the RoPE
+// position of a row is its rank in its level's candidate list, not its token
+// position; rows a query drops are not discarded but enter the same softmax,
+// as their node's mean value, next to the token rows it reaches. The explainer
+// page ("Recursive Sparse Attention RecSA: Million-Token Context Extrapolation
+// at Logarithmic Cost", section "Core Idea") describes the same descent: coarse
+// filtering near the root, refinement level by level down to the tokens.
 //
 // Per level (top to bottom):
 //   candidates  children of the nodes kept one level up (ascending), then the
@@ -42,6 +43,8 @@
 // to 128 VGPRs (4 waves per SIMD) for groups of up to 4 query heads.
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -65,32 +68,8 @@ __device__ __forceinline__ void load4(const void* base, int64_t off, float (&x)[
   }
 }
 
-struct Lds {
-  uint32_t q, qr, zs, sc, cid, flags, selA, selB, nls, bc, total;
-};
-
-__host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
-
-__host__ __device__ inline Lds lds_layout(int d, int G, int smax, int zcap) {
-  Lds L;
-  uint32_t o = 0;
-  L.q = o;     o = align16(o + 4u * G * d);         // raw query heads of the KV group
-  L.qr = o;    o = align16(o + 4u * G * d);         // rotated query operands of the current level
-  L.zs = o;    o = align16(o + 4u * G * zcap);      // logits, then softmax weights, [zcap][G]
-  L.sc = o;    o = align16(o + 4u * zcap);          // group scores
-  L.cid = o;   o = align16(o + 4u * zcap);          // node (or token) id of each scored candidate
-  L.flags = o; o = align16(o + zcap);               // kept flags
-  L.selA = o;  o = align16(o + 4u * smax);          // kept node ids, two buffers
-  L.selB = o;  o = align16(o + 4u * smax);
-  L.nls = o;   o = align16(o + 8u * (RECSA_MAX_LEVELS + 2));
-  L.bc = o;    o = align16(o + 4u * 2 * G);           // softmax rescale and sum, wave 0 -> all
-  L.total = o;
-  return L;
-}
-
-size_t attend_lds_bytes(int d, int G, int smax, int zcap) {
-  return lds_layout(d, G, smax, zcap).total;
-}
+typedef __bf16 mf_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float mf_f32x16_t __attribute__((ext_vector_type(16)));
 
 // Candidate index -> node (or token) id: children of the kept parents, then orphans.
 // Ids and indices fit in 32 bits (the capacity is at most INT32_MAX); a power-of-two
@@ -239,6 +218,146 @@ struct RawV {
   }
 };
 
+
+// The first scored level on the matrix cores (bf16 storage). A unit's first scored level holds all
+// n_l nodes of that level at their own index (every level above keeps all its nodes), so the units
+// of a workgroup whose first scored level is the same share its rotated keys: one tile
+// S = Q~ K~^T per 32 candidates on v_mfma_f32_32x32x16_bf16, the 32 rows being the units' query
+// heads rotated at their n_l (G rows per unit, zero rows past them) and the 32 columns 32
+// consecutive nodes rotated at their index. scale * S lands in each unit's logit array ([C][G]).
+// Every call path that scores this level (one wave per unit, several waves per unit, the decoding
+// step) takes its logits from this code, and the matrix core forms each output element from its
+// row and its column alone, so a unit's logits do not depend on which units share its workgroup.
+//
+// k-order: lane l supplies row (A) or column (B) l % 32 and the 8 elements of half kh = l / 32 of
+// each 16-wide k-step. Step m < D/32 takes the rotate-half "lo" elements QH kh + 8m + e (QH = D/4,
+// e < 8), step D/32 + m their partners HALF + QH kh + 8m + e: a lane rotates its own pairs in
+// registers (no lane exchange), and the D/16 steps take every element once.
+template <int D, int G>
+__device__ void mf_shared_levels(const AttnArgs& a, unsigned char* lds_all, const Lds& L, int slots, int slot, int ls,
+                                 int32_t cs, const float* qs, uint16_t* mstage, int64_t bh, int tid, int NT) {
+  constexpr int HALF = D / 2, QH = D / 4, MS = D / 32;
+  const int lane = static_cast<int>(threadIdx.x) % kWave, r32 = lane & 31, kh = lane >> 5;
+  const int nwaves = static_cast<int>(blockDim.x) / kWave, gw = static_cast<int>(threadIdx.x) / kWave;
+  auto info_of = [&](int s) { return reinterpret_cast<const int32_t*>(lds_all + s * L.total + L.info); };
+  int lv_hi = RECSA_MAX_LEVELS + 1;
+  for (;;) {
+    // the next (lower) first-scored level among the workgroup's units, and its largest node count
+    int L0 = 0;
+    int32_t cmax = 0;
+    for (int s = 0; s < slots; ++s) {
+      const int l = info_of(s)[0];
+      if (l < lv_hi && l > L0) L0 = l;
+    }
+    if (L0 == 0) break;
+    for (int s = 0; s < slots; ++s)
+      if (info_of(s)[0] == L0 && info_of(s)[1] > cmax) cmax = info_of(s)[1];
+    // this unit's G rows: its query heads rotated at its node count and rounded to bf16 (the
+    // rotation of the per-unit scoring, element for element); zeros when its level is another one
+    const bool mine = ls == L0;
+    for (int i = tid; i < G * HALF; i += NT) {
+      const int hh = i / HALF, p = i % HALF;
+      const float ql = qs[hh * D + p], qh = qs[hh * D + HALF + p];
+      float lo = 0.0f, hi = 0.0f;
+      if (mine) {
+        if (a.use_rope) {
+          const float2 t = a.tab[static_cast<int64_t>(cs) * HALF + p];
+          const float p1 = ql * t.x, p2 = qh * t.y;
+          const float p3 = qh * t.x, p4 = ql * t.y;
+          lo = p1 - p2;
+          hi = p3 + p4;
+        } else {
+          lo = ql;
+          hi = qh;
+        }
+      }
+      const uint32_t wd = __builtin_bit_cast(uint32_t, pack_bf16_rne(lo, hi));
+      uint16_t* row = mstage + (slot * G + hh) * D;
+      row[p] = static_cast<uint16_t>(wd & 0xFFFFu);
+      row[HALF + p] = static_cast<uint16_t>(wd >> 16);
+    }
+    for (int i = static_cast<int>(threadIdx.x); i < (32 - slots * G) * D / 8; i += static_cast<int>(blockDim.x))
+      reinterpret_cast<uint4*>(mstage + slots * G * D)[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    const uint16_t* arow = mstage + r32 * D + QH * kh;   // this lane's A fragments, read per k-step
+    const int64_t rowbase = bh * a.tree.rows[L0];
+    const uint16_t* src = static_cast<const uint16_t*>(a.tree.NK[L0]);
+    for (int cb = gw; cb * 32 < cmax; cb += nwaves) {
+      const int32_t c = cb * 32 + r32;
+      const int64_t cr = c < cmax ? c : cmax - 1;   // a column past the last node loads the last one
+      mf_f32x16_t acc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+      for (int m = 0; m < MS; ++m) {
+        const uint16_t* rp = src + (rowbase + cr) * D + QH * kh + 8 * m;
+        const uint4 ulo = *reinterpret_cast<const uint4*>(rp);
+        const uint4 uhi = *reinterpret_cast<const uint4*>(rp + HALF);
+        const uint32_t wl[4] = {ulo.x, ulo.y, ulo.z, ulo.w}, wh[4] = {uhi.x, uhi.y, uhi.z, uhi.w};
+        float klo[8], khi[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          klo[2 * q] = __uint_as_float(wl[q] << 16);
+          klo[2 * q + 1] = __uint_as_float(wl[q] & 0xFFFF0000u);
+          khi[2 * q] = __uint_as_float(wh[q] << 16);
+          khi[2 * q + 1] = __uint_as_float(wh[q] & 0xFFFF0000u);
+        }
+        float olo[8], ohi[8];
+        if (a.use_rope) {
+          const float4* t = reinterpret_cast<const float4*>(a.tab + cr * HALF + QH * kh + 8 * m);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 tv = t[q];
+            const float cc[2] = {tv.x, tv.z}, ss[2] = {tv.y, tv.w};
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+              const int e = 2 * q + v;
+              const float p1 = klo[e] * cc[v], p2 = khi[e] * ss[v];
+              const float p3 = khi[e] * cc[v], p4 = klo[e] * ss[v];
+              olo[e] = p1 - p2;
+              ohi[e] = p3 + p4;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            olo[e] = klo[e];
+            ohi[e] = khi[e];
+          }
+        }
+        uint4 bl, bhv;
+        bl.x = __builtin_bit_cast(uint32_t, pack_bf16_rne(olo[0], olo[1]));
+        bl.y = __builtin_bit_cast(uint32_t, pack_bf16_rne(olo[2], olo[3]));
+        bl.z = __builtin_bit_cast(uint32_t, pack_bf16_rne(olo[4], olo[5]));
+        bl.w = __builtin_bit_cast(uint32_t, pack_bf16_rne(olo[6], olo[7]));
+        bhv.x = __builtin_bit_cast(uint32_t, pack_bf16_rne(ohi[0], ohi[1]));
+        bhv.y = __builtin_bit_cast(uint32_t, pack_bf16_rne(ohi[2], ohi[3]));
+        bhv.z = __builtin_bit_cast(uint32_t, pack_bf16_rne(ohi[4], ohi[5]));
+        bhv.w = __builtin_bit_cast(uint32_t, pack_bf16_rne(ohi[6], ohi[7]));
+        const mf_bf16x8_t alo = __builtin_bit_cast(mf_bf16x8_t, *reinterpret_cast<const uint4*>(arow + 8 * m));
+        const mf_bf16x8_t ahi = __builtin_bit_cast(mf_bf16x8_t, *reinterpret_cast<const uint4*>(arow + HALF + 8 * m));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, __builtin_bit_cast(mf_bf16x8_t, bl), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, __builtin_bit_cast(mf_bf16x8_t, bhv), acc, 0, 0, 0);
+      }
+      // lane l holds column c and rows 8 (v / 4) + 4 kh + v % 4 of the tile
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * kh + (v & 3);
+        const int s = r / G, hh = r % G;
+        if (s < slots) {
+          const int32_t* in = info_of(s);
+          if (in[0] == L0 && c < in[1]) {
+            float* zs = reinterpret_cast<float*>(lds_all + s * L.total + L.zs);
+            zs[c * G + hh] = acc[v] * a.scale;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    lv_hi = L0;
+  }
+}
+
 // NW waves per unit. NW = 1: one wave does everything. NW > 1 (few units, latency-bound):
 // the waves share the score passes, wave 0 alone selects, wave h mod NW computes query head
 // h's softmax weights, and each wave owns D / NW of the value dimensions with the same row-group accumulation
@@ -250,7 +369,7 @@ struct RawV {
 // branch (a kept row has weight 0, and adding 0 * v leaves the sum unchanged). Occupancy
 // does not matter with so few units, so these kernels may take up to 256 registers.
 template <int D, bool BF16, int G, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1 && G <= 4 ? 4 : 2))) void attend_kernel(AttnArgs args) {
+__global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1 && G <= 4 ? 4 : 2))) void attend_kernel(AttnArgs args) {
   // read the arguments in place: the per-level tables are indexed by a run-time level, and a
   // by-value copy of the struct would be placed in scratch memory
   (void)args;
@@ -269,9 +388,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
   static_assert(NW == 1 || SR % (8 * (kWave / (D / VE))) == 0, "a staging round holds whole 8-row residue steps");
   static_assert(VE % NW == 0, "waves split the value elements of a lane");
 
-  extern __shared__ __align__(16) unsigned char lds[];
+  // bf16 storage: the first level a unit scores holds every node of that level, in order, for
+  // every unit of the workgroup; its logits come from one matrix-core tile (see mf_level below)
+  constexpr bool MF = BF16;
+  extern __shared__ __align__(16) unsigned char lds_all[];
+  // NW = 1: a workgroup holds `slots` units, one wave each; NW > 1: one unit on NW waves
+  const int slots = NW == 1 && MF ? static_cast<int>(blockDim.x) / kWave : 1;
+  // wave-uniform: held in a scalar register, so the unit's LDS addresses stay scalar too
+  const int slot = NW == 1 && MF ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave) : 0;
   const int zcap = a.zcap;
   const Lds L = lds_layout(D, G, a.smax, zcap);
+  unsigned char* lds = lds_all + slot * L.total;   // this unit's region
   float* qs = reinterpret_cast<float*>(lds + L.q);
   // rotated query operands, [G][D/16 lane slots][16 words]: bf16 packs 8 pairs
   // (lo0,lo1), (lo2,lo3), .., (hi6,hi7) into words 0..7; float32 keeps lo0..lo7, hi0..hi7
@@ -284,7 +411,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
   int32_t* selB = reinterpret_cast<int32_t*>(lds + L.selB);
   int64_t* nls = reinterpret_cast<int64_t*>(lds + L.nls);
   float* bc = reinterpret_cast<float*>(lds + L.bc);   // wave 0 -> all: alpha[G], l[G]
-  uint4* vst = reinterpret_cast<uint4*>(lds + L.total);   // staged value rows (several waves)
+  int32_t* info = reinterpret_cast<int32_t*>(lds + L.info);
+  uint4* vst = reinterpret_cast<uint4*>(lds_all + slots * L.total);   // staged value rows (several waves)
+  uint16_t* mstage = reinterpret_cast<uint16_t*>(lds_all + slots * L.total);   // matrix-core rows (same region)
   const bool staged = NW > 1 && a.pv_stage == 1;          // rounds of SR rows
   const bool prefetched = NW > 1 && a.pv_stage == 2;      // a chunk's rows, loaded while it is scored
   // the G logits (then weights) of candidate r: one vector LDS access
@@ -314,8 +443,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     }
   };
 
-  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int wid = NW == 1 ? 0 : static_cast<int>(threadIdx.x) / kWave;   // wave within the unit
+  const int tid = NW == 1 ? lane : static_cast<int>(threadIdx.x);         // thread within the unit
   constexpr int NT = NW * kWave;
   auto bsync = [&]() {
     if constexpr (NW == 1) wave_sync();
@@ -323,16 +453,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
   };
   const int sub = lane % RL, rg = lane / RL;       // value phase
   const int ssub = lane % SL, srg = lane / SL;     // score phase
-  const int64_t unit = blockIdx.x;
+  // units: per (sequence, KV head) its (query, selection group) pairs in order, `slots`
+  // consecutive ones per workgroup; consecutive workgroups take consecutive KV heads, so with 8
+  // KV heads every XCD keeps to one KV head (workgroup i runs on XCD i mod 8)
   const int64_t b = blockIdx.y;
-  const int64_t j = unit / a.Hkv;
-  const int h = static_cast<int>(unit % a.Hkv);
-  const int64_t n = a.prefill ? a.q_start + j + 1 : a.n_fixed;
+  const int hkv = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.Hkv_kv));
+  const int64_t u = static_cast<int64_t>(blockIdx.x / static_cast<unsigned>(a.Hkv_kv)) * slots + slot;
+  const bool active = u < a.n_q * a.kv_div;
+  const int64_t j = active ? u / a.kv_div : 0;
+  const int h = hkv * a.kv_div + static_cast<int>(u % a.kv_div);   // selection group
+  const int64_t n = !active ? 0 : a.prefill ? a.q_start + j + 1 : a.n_fixed;
   const int f = a.f;
-  const int64_t bh = b * a.Hkv_kv + h / a.kv_div;   // the selection group's KV head
+  const int64_t bh = b * a.Hkv_kv + hkv;
 
-  // raw query heads of the KV group -> LDS (float)
-  {
+  // raw query heads of the selection group -> LDS (float)
+  if (active) {
     const int64_t qbase = ((b * a.n_q + j) * a.Hq + static_cast<int64_t>(h) * G) * D;
     for (int i = tid * 4; i < G * D; i += NT * 4) {
       float x[4];
@@ -352,6 +487,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
   }
   bsync();
   const int T = static_cast<int>(nls[0]);
+  // the first level this unit scores: every level above it keeps all its nodes (k_l >= n_l), so
+  // its candidates are all of its n_l nodes, in order, at their own index; the query sits at n_l
+  int ls = 0;
+  int32_t cs = 0;
+  for (int lv = T; lv >= 1; --lv) {
+    const int32_t nl = static_cast<int32_t>(nls[lv]);
+    if (a.k.k[lv] < nl) {
+      ls = lv;
+      cs = nl;
+      break;
+    }
+  }
+  if constexpr (MF) {
+    if (tid == 0) {
+      info[0] = ls;
+      info[1] = cs;
+    }
+    __syncthreads();
+    mf_shared_levels<D, G>(a, lds_all, L, slots, slot, ls, cs, qs, mstage, bh, tid, NT);
+  }
+  if (!active) return;
   const int64_t sel_row0 = ((b * a.n_q + j) * a.Hkv + h) * a.n_levels;
   if (a.sel) {
     for (int lv = T + 1; lv <= a.n_levels; ++lv)
@@ -556,6 +712,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
       pass(r0 + NW * SPP, blo, bhi, tb, alo, ahi, ta);
     }
     bsync();
+  };
+  // the first scored level: its logits are already in zs (mf_shared_levels); the candidate -> node
+  // map, the group scores (the heads' logits summed in head order, as score_rows does) and, with
+  // several waves, the value prefetch
+  auto shared_rows = [&](const void* vsrc, int64_t rowbase, const CandMap& cm, int32_t cn) {
+    for (int32_t r = tid; r < cn; r += NT) {
+      cid[r] = cm(r);
+      float z[G];
+      zrow_load(r, z);
+      float S = 0.0f;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) S = S + z[hh];
+      sc[r] = S;
+    }
+    bsync();
+    if (prefetched) prefetch_values(vsrc, rowbase, cn);
   };
   // qpos >= 0: rotate the query heads at qpos first (a level's first chunk)
   auto score_rows = [&](const void* src, const void* vsrc, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn,
@@ -847,7 +1019,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
       bsync();
     } else {
       const int64_t rowbase = bh * a.tree.rows[lv];
-      score_rows(a.tree.NK[lv], a.tree.NV[lv], rowbase, cm, 0, C, C);
+      if (MF && lv == ls) shared_rows(a.tree.NV[lv], rowbase, cm, C);
+      else score_rows(a.tree.NK[lv], a.tree.NV[lv], rowbase, cm, 0, C, C);
       if (s > 0) {
         if (wid == 0) select_top(C, s, sel_new);
       } else {
@@ -919,10 +1092,32 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
 // GPU is not filled by one wave per unit and the descent's latency dominates.
 constexpr int64_t kMultiWaveUnits = 2048;
 
+// gfx950 has 160 KB of LDS per workgroup; a kernel's dynamic LDS limit is 64 KB until raised, and
+// the attribute belongs to the current device: raised once per device and instantiation
+constexpr size_t kLdsMax = 163840;
+
+template <int D, bool BF16, int G, int NW>
+static hipError_t allow_full_lds() {
+  constexpr int kDevices = 64;
+  static std::atomic<bool> done[kDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kDevices && done[dev].load()) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<D, BF16, G, NW>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsMax));
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kDevices) done[dev].store(true);
+  return hipSuccess;
+}
+
 template <int D, bool BF16, int G>
 static hipError_t launch_attend_t(const AttnArgs& a, size_t lds, int64_t B, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.n_q * a.Hkv), static_cast<unsigned>(B));
-  if (a.n_q * a.Hkv * B < kMultiWaveUnits) {
+  // units per (sequence, KV head): its queries times its selection groups
+  const int64_t units_kv = a.n_q * a.kv_div;
+  const size_t mf = BF16 ? mf_stage_bytes(D) : 0;   // the matrix-core tile's rows
+  if (units_kv * a.Hkv_kv * B < kMultiWaveUnits) {
+    const dim3 grid(static_cast<unsigned>(units_kv * a.Hkv_kv), static_cast<unsigned>(B));
     // value rows through LDS when it has room: a whole chunk's rows (zcap of them, rounded up
     // to whole 8-row residue steps -- 8 * 64 / (D / 4) rows -- then to whole 64-lane loads of
     // 16 bytes), prefetched while the chunk is scored; else rounds of 4 waves x 64 lanes x 4
@@ -932,19 +1127,32 @@ static hipError_t launch_attend_t(const AttnArgs& a, size_t lds, int64_t B, hipS
     const size_t rows = (static_cast<size_t>(a.zcap) + kStep - 1) / kStep * kStep;
     const size_t kFull = (rows * kPiecesPerRow + kWave - 1) / kWave * kWave * 16;
     constexpr size_t kStage = 4 * kWave * 4 * 16;
-    if (lds + kFull <= 65536) {
+    hipError_t e = allow_full_lds<D, BF16, G, 4>();
+    if (e != hipSuccess) return e;
+    // the staged value rows and the tile's rows share one region (the tile is done first)
+    if (lds + std::max(kFull, mf) <= 65536) {
       AttnArgs b = a;
       b.pv_stage = 2;
-      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + kFull, s, b);
-    } else if (lds + kStage <= 65536) {
+      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + std::max(kFull, mf), s, b);
+    } else if (lds + std::max(kStage, mf) <= 65536) {
       AttnArgs b = a;
       b.pv_stage = 1;
-      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + kStage, s, b);
+      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + std::max(kStage, mf), s, b);
     } else {
-      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds, s, a);
+      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + mf, s, a);
     }
   } else {
-    hipLaunchKernelGGL((attend_kernel<D, BF16, G, 1>), grid, dim3(kWave), lds, s, a);
+    // bf16: up to 8 units of one KV head per workgroup, one wave each, whose rows fill the 32
+    // rows of the first scored level's tile, as many as LDS holds; float32: one unit
+    int slots = BF16 ? std::min(8, 32 / G) : 1;
+    while (slots > 1 && slots * lds + mf > kLdsMax) slots /= 2;
+    const size_t bytes = slots * lds + mf;
+    if (bytes > 65536) {
+      hipError_t e = allow_full_lds<D, BF16, G, 1>();
+      if (e != hipSuccess) return e;
+    }
+    const dim3 grid(static_cast<unsigned>((units_kv + slots - 1) / slots * a.Hkv_kv), static_cast<unsigned>(B));
+    hipLaunchKernelGGL((attend_kernel<D, BF16, G, 1>), grid, dim3(slots * kWave), bytes, s, a);
   }
   return hipGetLastError();
 }

@@ -1,9 +1,9 @@
 // Tree build: pooled node keys and mean node values, one level per launch.
 //
 // RecSA abstract ("Recursive Sparse Attention: Million-Token Length
-// Extrapolation at Logarithmic Cost"): every node summarises its subtree with
-// one key from the layer's pooler, shared by all levels, and one mean-pooled
-// value. Here the pooler is key = W @ m, m the mean of the node's f children's
+// Extrapolation at Logarithmic Cost"): a node stores a key made by the layer's
+// pooler (the same pooler at every level) and a value averaged over its span.
+// Here the pooler is key = W @ m, m the mean of the node's f children's
 // stored keys; the value is the mean of the children's stored values.
 //
 // HBM-bound: a tile reads f * (nodes per tile) child rows of K and V once and
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(512, 4) void pool_kernel(PoolArgs a) {
   }
 }
 
-int pool_nodes_per_tile(int d) { return d == 128 ? PoolGeom<128>::NPW : PoolGeom<64>::NPW; }
+static_assert(PoolGeom<128>::NPW == 32 && PoolGeom<64>::NPW == 64, "pool_nodes_per_tile (sizing.hpp)");
 
 static int persistent_grid() {
   static int cus = 0;

@@ -134,7 +134,7 @@ struct DenseGeom {
   static constexpr int QPB = 4 * QPW;  // queries per workgroup
 };
 
-int dense_queries_per_block(int G) { return 4 * (32 / G); }
+
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 

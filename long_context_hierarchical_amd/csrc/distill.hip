@@ -12,7 +12,7 @@
 
 namespace recsa {
 
-constexpr int kLossBlocks = 1024;
+
 
 // dout = 2 (out - target) / N; partial[block] = sum of (out - target)^2 over the block's
 // grid-stride elements (fixed order within a thread, then the block's fixed reduction)
@@ -50,10 +50,6 @@ __global__ __launch_bounds__(256) void distill_update_kernel(float* Wm, const fl
   store1<BF16>(W, i, round_store<BF16>(w));
 }
 
-int distill_loss_blocks(int64_t n) {
-  const int64_t b = (n + 255) / 256;
-  return static_cast<int>(b < kLossBlocks ? b : kLossBlocks);
-}
 
 hipError_t launch_distill_loss(const float* out, const float* target, float* dout, float* partial, float* loss,
                                int64_t n, hipStream_t s) {

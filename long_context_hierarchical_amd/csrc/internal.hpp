@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "recsa.h"
+#include "sizing.hpp"
 
 namespace recsa {
 
@@ -29,8 +30,6 @@ struct PoolArgs {
   int64_t dst2_rows;
   int32_t grid;         // persistent grid size (0 = library default)
 };
-// Nodes per tile of the pool kernel (the next level is fused when the fanout divides it).
-int pool_nodes_per_tile(int d);
 hipError_t launch_pool_level(const PoolArgs& a, int d, bool bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- RoPE table
@@ -103,7 +102,6 @@ struct AttnArgs {
   TreeLevels tree;
 };
 
-size_t attend_lds_bytes(int d, int G, int smax, int zcap);
 
 // ---------------------------------------------------------------- gradients (selections held fixed)
 struct BwdArgs {
@@ -158,7 +156,6 @@ hipError_t launch_tree_push(const TreePushArgs& a, int d, bool bf16, hipStream_t
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
 // ---------------------------------------------------------------- pooler distillation
-int distill_loss_blocks(int64_t n);
 // dout = 2 (out - target) / n and loss = mean of (out - target)^2 (partial: distill_loss_blocks(n) floats)
 hipError_t launch_distill_loss(const float* out, const float* target, float* dout, float* partial, float* loss,
                                int64_t n, hipStream_t s);
@@ -189,8 +186,6 @@ struct DenseArgs {
   int32_t use_rope;
   InvFreq iv;
 };
-// Query rows per workgroup of the dense kernel (G query heads of one KV head per query).
-int dense_queries_per_block(int G);
 hipError_t launch_dense(const DenseArgs& a, int d, bool bf16, int G, int64_t B, hipStream_t s);
 // bf16 queries rotated at their positions into qr ([B][n_q][H_q][d], bf16), for the MFMA kernel.
 hipError_t launch_rotate_queries(const DenseArgs& a, void* qr, int64_t B, int d, hipStream_t s);
@@ -261,7 +256,7 @@ __host__ __device__ inline TsTokenLayout ts_token_layout(int d, int G, int64_t C
   return L;
 }
 // LDS of the merge workgroup: the merged list (scores, ids) and a histogram.
-size_t ts_merge_lds_bytes(int64_t merge);
+inline size_t ts_merge_lds_bytes(int64_t merge) { return static_cast<size_t>(2 * ts_al16(merge * 4) + 256 * 4); }
 
 // q1[row] = round(rot(q[row], p1)), q0[row] = round(rot(q[row], p0)) for rows = B n_q H_q (copies
 // without rotation).

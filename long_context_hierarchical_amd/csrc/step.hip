@@ -2,9 +2,9 @@
 // its arrival completes are built (the attention that follows is attend.hip's kernel).
 //
 // RecSA abstract ("Recursive Sparse Attention: Million-Token Length Extrapolation at
-// Logarithmic Cost"): the tree is kept over the KV cache, each node summarising its subtree
-// with one pooled key (the layer's pooler, shared by all levels) and one mean-pooled value;
-// decoding reads O(log L) entries per step. Here the pooler is key = W @ m, m the mean of the
+// Logarithmic Cost"): the tree lives over the KV cache; a node holds a key from the layer's
+// pooler (one pooler for every level) and the average of the values it spans, and a decoding
+// step touches a number of rows that grows with the tree height only. Here the pooler is key = W @ m, m the mean of the
 // node's f children's stored keys, and the value is the mean of the children's stored values.
 #include "common.hpp"
 #include "internal.hpp"

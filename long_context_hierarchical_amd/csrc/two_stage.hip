@@ -719,7 +719,7 @@ static void ts_tokens_t(const TsArgs& a, bool bf16, size_t lds, hipStream_t s) {
   else hipLaunchKernelGGL((ts_token_kernel<D, false, G>), grid, dim3(256), lds, s, a);
 }
 
-size_t ts_merge_lds_bytes(int64_t merge) { return static_cast<size_t>(2 * ts_al16(merge * 4) + 256 * 4); }
+
 
 hipError_t launch_ts_merge(const TsArgs& a, hipStream_t s) {
   if (a.n_q <= 0 || a.s1 <= 0) return hipSuccess;

@@ -7,6 +7,7 @@ missing; nothing here is a fallback.
 """
 from .recsa import (  # noqa: F401
     INT32_MAX,
+    TreeCache,
     UnitResult,
     attend_unit,
     bf16_round,

@@ -19,7 +19,8 @@ _lib = None
 
 
 def build() -> str:
-    tmp = LIB + ".tmp"
+    # a private temporary name per process: parallel test workers may all build at once
+    tmp = f"{LIB}.tmp{os.getpid()}"
     subprocess.run(["gcc", *CFLAGS, *SRC, "-o", tmp, "-lm"], check=True)
     os.replace(tmp, LIB)
     return LIB

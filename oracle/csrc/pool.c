@@ -2,8 +2,8 @@
  * RecSA oracle: node summaries (TEST INFRASTRUCTURE ONLY; the GPU library never uses this).
  *
  * "Recursive Sparse Attention: Million-Token Length Extrapolation at Logarithmic Cost",
- * abstract: a node summarises its subtree with one key from the layer's pooler and one
- * mean-pooled value. Reading: key = W m, m = mean of the f children's stored keys; value =
+ * abstract: a node holds a key produced by the layer's pooler and the average of the
+ * values below it. Reading: key = W m, m = mean of the f children's stored keys; value =
  * mean of the children's stored values; both rounded to the storage type.
  *
  * Arithmetic, written out so that every rounding is visible:

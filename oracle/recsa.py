@@ -13,13 +13,14 @@ Sources, cited by page title and section:
   [Position]  the same page -- section "Position Encoding Ingenuity: Making
               Extrapolation Possible".
 
-What the pages fix: a tree over the KV cache whose nodes each carry one
-pooled key and the mean of the subtree's values [Abstract, Core Idea]; one
-pooler per layer for every level [Abstract]; a query descends level by level
-and keeps at most k candidates per level above the tokens [Abstract, Core
-Idea]; the summaries of the candidates it does not keep share one softmax
-with the exact tokens [Abstract]; an entry's RoPE position is its index among
-the candidates of its level [Abstract, Position].
+What the pages fix: a tree is kept over the KV cache, a node holding a
+pooled key and the average of the values below it [Abstract, Core Idea]; the
+same pooler serves every level of a layer [Abstract]; going down the tree a
+query retains no more than k candidates at each level above the tokens
+[Abstract, Core Idea]; the summaries it drops are not lost but are weighted in
+the same softmax as the token rows it reaches [Abstract]; RoPE is applied at a
+row's rank within its level's candidate list rather than at its token
+position [Abstract, Position].
 
 Readings where the pages are silent (all are listed in the design notes):
 complete-node forest with orphans and an exact trailing block; pooler
@@ -123,9 +124,9 @@ def plan_counts(n: int, f: int, k_levels, self_in: bool = False):
 def pool_nodes(cK: np.ndarray, cV: np.ndarray, W: np.ndarray, f: int, dtype: str):
     """Summaries of g complete nodes from their stored children, in child order.
 
-    [Abstract]: each node summarises its subtree with one key from the layer's
-    pooler and one mean-pooled value; [Core Idea]: a node's value is the mean
-    of its subtree's token values. Reading: key = W @ m with m the mean of the
+    [Abstract]: a node carries a key produced by the layer's pooler and a value
+    that averages what lies below it; [Core Idea]: that value is the average of
+    the token values of the node's span. Reading: key = W @ m with m the mean of the
     f child keys; value = mean of the f stored child values (equal to the
     subtree mean for a complete subtree).
 
@@ -147,7 +148,7 @@ def build_slice(K: np.ndarray, V: np.ndarray, W: np.ndarray, f: int, dtype: str,
     K, V: [>= n_new, d] float32 token rows (pre-RoPE); W: [d, d] float32.
     tree: list over levels l = 1.. of (NK_l, NV_l) float32 arrays sized floor(cap / f^l);
     nodes already present are never changed. Level l >= 2 pools the stored
-    level l-1 nodes with the same pooler [Abstract: shared by all levels].
+    level l-1 nodes with the same pooler [Abstract: one pooler for every level].
     """
     d = K.shape[1]
     cap = n_new if cap is None else cap
@@ -242,14 +243,16 @@ class UnitResult:
     flags: dict = field(default_factory=dict)     # level -> near tie at the selection boundary
     C: dict = field(default_factory=dict)         # level -> candidate count (level 0 included)
     entries: list = field(default_factory=list)   # (level, node or token id) per softmax entry
-    epos: list = field(default_factory=list)      # each entry's index among its level's candidates
+    epos: list = field(default_factory=list)      # each entry's rank in its level's candidate list
     z: np.ndarray | None = None                   # [E, G] float32 logits of the entries
     weights: np.ndarray | None = None             # [E, G] float64 softmax weights
     q_pos: dict = field(default_factory=dict)     # level -> query RoPE position
+    scores: dict = field(default_factory=dict)    # level -> (candidate ids, float64 group scores)
 
 
 def attend_unit(q: np.ndarray, K: np.ndarray, V: np.ndarray, tree, n: int, f: int, k_levels,
-                dtype: str, theta: float = 1.0e6, scale=None, self_in: bool = False) -> UnitResult:
+                dtype: str, theta: float = 1.0e6, scale=None, self_in: bool = False,
+                fixed_sel: dict | None = None) -> UnitResult:
     """One query token against one KV head's cache of n tokens (RecSA descent + one softmax).
 
     q: [G, d] float32 (the G query heads sharing this KV head); K, V: [>= n, d]
@@ -264,6 +267,12 @@ def attend_unit(q: np.ndarray, K: np.ndarray, V: np.ndarray, tree, n: int, f: in
     candidates with the highest group score are kept, the others become
     softmax entries with their mean values; at the token level every
     candidate token is an entry. One softmax over all entries per head.
+
+    fixed_sel {level: node ids}: the kept set of those levels is taken as given
+    instead of chosen by score (forced-selection replay: where two sides split a
+    near tie differently, the levels below are compared with one side's choice
+    imposed on the other). A given set must hold min(k_l, C_l) distinct
+    candidates of that level.
     """
     G, d = q.shape
     scale32 = default_scale(d) if scale is None else _F32(scale)
@@ -289,9 +298,17 @@ def attend_unit(q: np.ndarray, K: np.ndarray, V: np.ndarray, tree, n: int, f: in
         NK, NV = tree[lv - 1]
         z = _logits(q, NK[cand], C, dtype, theta, scale32)             # [G, C]
         S = z.astype(_F64).sum(axis=0)
+        res.scores[lv] = (cand, S)
         order = np.lexsort((np.arange(C), -S))                          # S desc, index asc
         res.flags[lv] = bool(0 < s < C and
                              0.0 < S[order[s - 1]] - S[order[s]] < NEAR_TIE_REL * np.abs(S).max())
+        if fixed_sel is not None and lv in fixed_sel:
+            pos = {int(c): i for i, c in enumerate(cand)}
+            want = sorted(int(x) for x in fixed_sel[lv])
+            if len(want) != s or len(set(want)) != s or any(x not in pos for x in want):
+                raise ValueError(f"fixed selection at level {lv} is not {s} distinct candidates")
+            keep = np.array([pos[x] for x in want], dtype=np.int64)
+            order = np.concatenate([keep, np.setdiff1d(np.arange(C), keep)])
         chosen = np.sort(order[:s])
         res.sel[lv] = [int(cand[i]) for i in chosen]
         for i in np.sort(order[s:]):

@@ -34,8 +34,9 @@ def rot(x: np.ndarray, p: int, theta: float) -> np.ndarray:
 
 def brute_unit(q, K, V, W, n, f, k_levels, theta=1.0e6, scale=None, self_in=False, fixed_sel=None):
     """Returns dict(out [G,d], lse [G], sel {level: sorted ids}, gap {level: relative boundary gap},
-    entries [(level, id)]). fixed_sel {level: kept ids} replaces the selection by scores (the
-    function of q, K, V and W that gradients with held selections differentiate)."""
+    entries [(level, id)]). fixed_sel {level: kept ids} replaces the selection by scores at the
+    levels it lists (with every level listed: the function of q, K, V and W that gradients with
+    held selections differentiate)."""
     q = np.asarray(q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -61,8 +62,8 @@ def brute_unit(q, K, V, W, n, f, k_levels, theta=1.0e6, scale=None, self_in=Fals
             z = np.array([sc * np.dot(rot(q[h], C, theta), rot(key, i, theta)) for h in range(G)])
             zmap[g] = z
             S[g] = z.sum()
-        if fixed_sel is not None:
-            kept = set(fixed_sel.get(lv, []))
+        if fixed_sel is not None and lv in fixed_sel:
+            kept = set(fixed_sel[lv])
             rest = [i for i in range(C) if cands[i] not in kept]
         else:
             s = min(int(k_levels[lv - 1]), C)

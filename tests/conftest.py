@@ -12,3 +12,10 @@ for _p in (ROOT, os.path.join(ROOT, "tests")):
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # worker processes of the full-size tests' oracle pool, if any were started
+    mod = sys.modules.get("oracle_pool")
+    if mod is not None:
+        mod.shutdown()

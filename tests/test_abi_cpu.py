@@ -4,10 +4,11 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from long_context_hierarchical_amd import recsa as R
-from oracle import level_counts, plan_counts
+from oracle import INT32_MAX, level_counts, plan_counts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -61,6 +62,24 @@ def test_sel_width_matches_closed_form(n, f, k):
         _, sm, _ = plan_counts(m, f, ks + [k] * 4)
         want = max(want, max(sm.values(), default=0))
     assert R.recsa_sel_width(sh, lo, n, ks) == want
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sel_width_over_ranges_matches_every_prefix(seed):
+    """recsa_sel_width(n_min, n_max) = the largest kept count over every prefix in the range, with
+    per-level k that make the kept counts rise and fall with n (orphans, levels kept whole)."""
+    rng = np.random.default_rng(seed)
+    f = int(rng.choice([2, 3, 4, 16]))
+    n_max = int(rng.integers(1, 3000))
+    n_min = int(rng.integers(0, n_max + 1))
+    T = R.recsa_num_levels(n_max, f)
+    ks = [int(rng.choice([0, 1, 2, 3, 5, 17, INT32_MAX])) for _ in range(max(T, 1))]
+    sh = _shape(fanout=f, capacity=n_max)
+    want = 0
+    for m in range(n_min, n_max + 1):
+        _, sm, _ = plan_counts(m, f, ks + [ks[-1]] * 4)
+        want = max(want, max(sm.values(), default=0))
+    assert R.recsa_sel_width(sh, n_min, n_max, ks) == want
 
 
 def test_workspace_holds_the_rope_table():

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import gpu_util
-from gpu_util import TOL, Gpu, compare_unit, storage_bits
+from gpu_util import TOL, Gpu, check_unit, oracle_replayer, storage_bits
 from long_context_hierarchical_amd import recsa as R
 from synthetic import WORKLOADS, Workload, gen_decode_inputs, with_overrides
 
@@ -21,20 +21,29 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _check_units(w, inp, res, k, units, mode, n_tokens=None, q_start=0, min_match=0.9):
+def _check_units(w, inp, res, k, units, mode, n_tokens=None, q_start=0):
+    """Every unit's selections, outputs and lse against the oracle; a near-tie split is followed
+    by forced-selection replay, so no unit goes unchecked."""
     out, lse, sel, _ = res
+    cache = oracle.TreeCache(inp["K"], inp["V"], inp["W"], w.f, w.dtype)
     if mode == "decode":
-        ref = oracle.decode(inp["K"], inp["V"], inp["W"], inp["q"], n_tokens, w.f, k, w.dtype, w.theta, units=units)
+        qs = inp["q"]
+        ref = oracle.decode(inp["K"], inp["V"], inp["W"], qs, n_tokens, w.f, k, w.dtype, w.theta, units=units,
+                            cache=cache)
     else:
         qs = inp["q"][:, q_start:q_start + out.shape[1]]
-        ref = oracle.prefill(inp["K"], inp["V"], inp["W"], qs, q_start, w.f, k, w.dtype, w.theta, units=units)
+        ref = oracle.prefill(inp["K"], inp["V"], inp["W"], qs, q_start, w.f, k, w.dtype, w.theta, units=units,
+                             cache=cache)
     G = w.G
-    stats = {"match": 0, "excused": 0}
+    stats = {"match": 0, "replayed": 0}
     for (b, j, h), r in ref.items():
-        st = compare_unit(r, sel[b, j, h], out[b, j, h * G:(h + 1) * G], lse[b, j, h * G:(h + 1) * G],
-                          TOL[w.dtype], where=f"{w.name} unit {(b, j, h)}")
+        n = n_tokens if mode == "decode" else q_start + j + 1
+        rep = oracle_replayer(cache, qs, w, k, b, j, h, n, mode != "decode")
+        st = check_unit(r, sel[b, j, h], out[b, j, h * G:(h + 1) * G], lse[b, j, h * G:(h + 1) * G],
+                        TOL[w.dtype], where=f"{w.name} unit {(b, j, h)}", replay=rep)
         stats[st] += 1
-    assert stats["match"] >= min_match * len(ref), stats
+    if stats["replayed"]:
+        _say(f"{w.name}: {stats}")
     return stats
 
 
@@ -115,7 +124,7 @@ def test_decode_tiny_workload_full():
     k = [w.k] * 3
     res = g.decode(k, w.L)
     units = [(0, j, 0) for j in range(w.n_queries)]
-    _check_units(w, inp, res, k, units, "decode", n_tokens=w.L, min_match=1.0)
+    _check_units(w, inp, res, k, units, "decode", n_tokens=w.L)
 
 
 DECODE_CASES = [
@@ -306,18 +315,102 @@ def test_heads_selecting_in_smaller_groups(Gs, mode):
     out = torch.empty(w.B, n_q, w.Hq, w.d, dtype=torch.float32, device=dev)
     lse = torch.empty(w.B, n_q, w.Hq, dtype=torch.float32, device=dev)
     sel = torch.full((w.B, n_q, groups, T, width), -7, dtype=torch.int32, device=dev)
+    cache = oracle.TreeCache(inp["K"], inp["V"], inp["W"], w.f, w.dtype)
     if mode == "prefill":
         R.recsa_prefill(sh, q, q_start, K, V, tree, k, out, lse, sel, width, ws)
-        ref = oracle.prefill(inp["K"], inp["V"], inp["W"], inp["q"], q_start, w.f, k, w.dtype, w.theta, select_heads=Gs)
+        ref = oracle.prefill(inp["K"], inp["V"], inp["W"], inp["q"], q_start, w.f, k, w.dtype, w.theta, select_heads=Gs,
+                             cache=cache)
     else:
         R.recsa_decode(sh, q, K, V, tree, w.L, k, out, lse, sel, width, ws)
-        ref = oracle.decode(inp["K"], inp["V"], inp["W"], inp["q"], w.L, w.f, k, w.dtype, w.theta, select_heads=Gs)
+        ref = oracle.decode(inp["K"], inp["V"], inp["W"], inp["q"], w.L, w.f, k, w.dtype, w.theta, select_heads=Gs,
+                            cache=cache)
     torch.cuda.synchronize()
     out, lse, sel = out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
-    stats = {"match": 0, "excused": 0}
+    stats = {"match": 0, "replayed": 0}
     for (b, j, g), r in ref.items():
-        st = compare_unit(r, sel[b, j, g], out[b, j, g * Gs:(g + 1) * Gs], lse[b, j, g * Gs:(g + 1) * Gs],
-                          TOL[w.dtype], where=f"select_heads {Gs} unit {(b, j, g)}")
+        n = q_start + j + 1 if mode == "prefill" else w.L
+        rep = oracle_replayer(cache, inp["q"], w, k, b, j, g, n, mode == "prefill", Gs=Gs)
+        st = check_unit(r, sel[b, j, g], out[b, j, g * Gs:(g + 1) * Gs], lse[b, j, g * Gs:(g + 1) * Gs],
+                        TOL[w.dtype], where=f"select_heads {Gs} unit {(b, j, g)}", replay=rep)
         stats[st] += 1
     _say(f"select_heads {Gs} {mode}: {stats}")
-    assert stats["match"] >= 0.9 * len(ref)
+
+
+# ------------------------------------------------------------------ exact ties
+
+def _tie_inputs(kind, B, Hkv, Hq, d, L, dtype, seed, n_q):
+    """Inputs whose group scores tie exactly at the selection boundary of every level.
+    'zero': every key is 0, so every logit is 0 (the lowest-index candidates must be kept).
+    'blocks': rotation off; the keys repeat whole f^2-token blocks drawn from three vectors, so
+    every level-1 node under such a block has the same key and the level-2 nodes take three
+    values: runs of equal scores straddle the k-th place at levels 1 and 2."""
+    rng = np.random.default_rng(seed)
+    std = 1.0 if dtype == "f32" else d ** -0.5
+
+    def store(x):
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        if dtype == "bf16":
+            from synthetic import bf16_bits
+            return bf16_bits(x)
+        return x
+    if kind == "zero":
+        K = np.zeros((B, Hkv, L, d), np.float32)
+    else:
+        base = rng.standard_normal((B, Hkv, 3, d)).astype(np.float32) * std
+        pick = rng.integers(0, 3, (B, Hkv, -(-L // 256)))
+        K = np.take_along_axis(base, np.repeat(pick, 256, axis=2)[..., :L, None].repeat(d, 3), axis=2)
+    V = rng.standard_normal((B, Hkv, L, d)).astype(np.float32) * std
+    q = rng.standard_normal((B, n_q, Hq, d)).astype(np.float32) * std
+    W = (np.eye(d) + 0.05 / np.sqrt(d) * rng.standard_normal((d, d))).astype(np.float32)
+    return {"K": store(K), "V": store(V), "q": store(q), "W": store(W)}
+
+
+TIE_CASES = [
+    # (kind, dtype, d, G, f, L, k per level)
+    ("zero", "bf16", 128, 4, 16, 16 ** 3 * 2 + 77, [8, 8, 8]),
+    ("zero", "f32", 64, 4, 16, 16 ** 3 + 300, [3, 20, 1]),
+    ("zero", "bf16", 128, 8, 32, 32 ** 3 + 32 ** 2 + 50, [16, 20, 2]),  # level 1: 640 candidates
+    ("zero", "bf16", 64, 2, 16, 4500, [0, 8, 16]),
+    ("blocks", "bf16", 128, 4, 16, 16 ** 3 * 3 + 5, [8, 5, 8]),
+    ("blocks", "f32", 64, 4, 16, 16 ** 3 + 19, [4, 7, 2]),
+    ("blocks", "bf16", 128, 8, 16, 16 ** 3 * 2, [12, 20, 3]),
+]
+
+
+@pytest.mark.parametrize("case", TIE_CASES, ids=lambda c: f"{c[0]}_{c[1]}_d{c[2]}_G{c[3]}_f{c[4]}")
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_exact_ties_keep_lowest_indices(case, mode):
+    """Equal group scores at the k-th place: the kept sets must be exactly the oracle's (equal
+    scores go to the lower candidate index); no near-tie allowance applies to exact ties."""
+    kind, dtype, d, G, f, L, k = case
+    Hkv, n_q = 2, 4
+    w = _w(f"tie_{kind}", B=1, Hq=G * Hkv, Hkv=Hkv, d=d, dtype=dtype, L=L, f=f, k=k[0], n_queries=n_q,
+           theta=(1.0e6 if kind == "zero" else 0.0), seed=91)
+    inp = _tie_inputs(kind, 1, Hkv, G * Hkv, d, L, dtype, 91, n_q if mode == "decode" else L)
+    g = Gpu(w, inp)
+    T = R.recsa_num_levels(L, f)
+    kk = (k + [k[-1]] * T)[:T]
+    if mode == "decode":
+        res = g.decode(kk, L)
+        units = [(0, j, h) for j in range(n_q) for h in range(Hkv)]
+        ref = oracle.decode(inp["K"], inp["V"], inp["W"], inp["q"], L, f, kk, dtype, w.theta, units=units)
+    else:
+        q_start = L - 300
+        res = g.prefill(kk, q_start, 300)
+        pos = [0, 1, 2, 15, 16, 17, 100, 255, 256, 299]
+        units = [(0, p, h) for p in pos for h in range(Hkv)]
+        ref = oracle.prefill(inp["K"], inp["V"], inp["W"], inp["q"][:, q_start:], q_start, f, kk, dtype, w.theta,
+                             units=units)
+    out, lse, sel, _ = res
+    ties = 0
+    for (b, j, h), r in ref.items():
+        for lv in range(1, len(r.sel) + 1):
+            cand, S = r.scores.get(lv, (None, None))
+            s = len(r.sel[lv])
+            if S is not None and 0 < s < len(S):
+                Ss = np.sort(S)[::-1]
+                ties += Ss[s - 1] == Ss[s]
+        st, _fx = gpu_util.compare_unit(r, sel[b, j, h], out[b, j, h * G:(h + 1) * G], lse[b, j, h * G:(h + 1) * G],
+                                        TOL[dtype], where=f"ties {case} {mode} unit {(b, j, h)}")
+        assert st == "match"
+    assert ties > 0, "no level had an exact tie at its boundary"

@@ -113,17 +113,62 @@ def test_no_pruning_equals_textbook_dense(dtype, tol, mode, f):
     np.testing.assert_allclose(r.out, do, rtol=0, atol=1e-12)
 
 
-def test_dense_oracle_matches_textbook_long_positions():
-    """The dense comparator at positions near 2M (f32): rotation angles far beyond 2*pi."""
+def _dense_textbook_vec(q, K, V, n_keys, q_pos, theta):
+    """Textbook RoPE attention in float64, vectorised for long caches: the pairs (x_i, x_{i+d/2})
+    as complex numbers turned by exp(i p omega_i) at float64 angles (omega_i as the build keeps
+    them, float32), softmax through logsumexp."""
+    from scipy.special import logsumexp
+    d = q.shape[1]
+    h = d // 2
+    om = (np.float32(theta) ** (-(2.0 * np.arange(h)) / d)).astype(np.float32).astype(np.float64)
+    Kc = (K[:n_keys, :h] + 1j * K[:n_keys, h:]).astype(np.complex128) * np.exp(1j * np.arange(n_keys)[:, None] * om)
+    qc = (q[:, :h] + 1j * q[:, h:]).astype(np.complex128) * np.exp(1j * float(q_pos) * om)
+    Z = (qc.real @ Kc.real.T + qc.imag @ Kc.imag.T) / np.sqrt(d)   # Re(q conj(k)) = <rot q, rot k>
+    lse = logsumexp(Z, axis=1)
+    return np.exp(Z - lse[:, None]) @ V[:n_keys].astype(np.float64), lse
+
+
+@pytest.mark.parametrize("dtype,tol", [("f32", 1e-6), ("bf16", 2e-3)])
+def test_dense_oracle_matches_textbook_long_positions(dtype, tol):
+    """The dense comparator over 2^21 + 37 keys, the query at 2^21 + 37: angles of up to 2M rad,
+    where a float32 angle (ulp 0.125 rad) or a float32 inverse frequency applied in float32 would
+    be visibly wrong. Against the float64 textbook; the oracle rounds its rotated keys and query
+    to the storage type, the textbook does not."""
     rng = np.random.default_rng(3)
-    d, G, n = 64, 4, 2100
-    K, V, q = _rand(rng, (n, d)), _rand(rng, (n, d)), _rand(rng, (G, d))
-    # shift positions by building the key array at the end of a long virtual cache
+    d, G, n = 8, 2, 2 ** 21 + 37
+    std = 1.0 if dtype == "f32" else d ** -0.5
+    K, V, q = _rand(rng, (n, d), std, dtype), _rand(rng, (n, d), std, dtype), _rand(rng, (G, d), 4 * std, dtype)
     theta = 1.0e6
-    out, lse = dense_unit(q, K, V, n, n, "f32", theta)
-    ref, rlse = dense_textbook(q, K, V, n, n, theta)
-    np.testing.assert_allclose(out, ref, atol=1e-6, rtol=0)
-    np.testing.assert_allclose(lse, rlse, atol=1e-5, rtol=0)
+    out, lse = dense_unit(q, K, V, n, n, dtype, theta)
+    ref, rlse = _dense_textbook_vec(q, K, V, n, n, theta)
+    np.testing.assert_allclose(out, ref, atol=tol, rtol=0)
+    np.testing.assert_allclose(lse, rlse, atol=10 * tol, rtol=0)
+    # the same pin on a short cache agrees with the per-key textbook
+    ref2, rl2 = dense_textbook(q, K, V, 300, 300, theta)
+    ref3, rl3 = _dense_textbook_vec(q, K, V, 300, 300, theta)
+    np.testing.assert_allclose(ref2, ref3, atol=1e-12, rtol=0)
+
+
+def test_dense_long_positions_catch_float32_angles():
+    """A planted mistake, on the CPU: the oracle's rotation with angles formed in float32 differs
+    from the float64 textbook at 2M positions by at least 100 times the float32 tolerance of the
+    pin above (1e-6), so that pin catches it."""
+    rng = np.random.default_rng(4)
+    d, G, n = 8, 2, 2 ** 21 + 37
+    K, V, q = _rand(rng, (n, d)), _rand(rng, (n, d)), _rand(rng, (G, d), 4.0)
+    from oracle import recsa as orc
+    saved = orc.rope_rows
+
+    def rope_rows_f32(pos, d, theta):
+        ang = np.asarray(pos, dtype=np.float32)[:, None] * orc.inv_freq(d, theta)[None, :]
+        return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    orc.rope_rows = rope_rows_f32
+    try:
+        out, _ = dense_unit(q, K, V, n, n, "f32", 1.0e6)
+    finally:
+        orc.rope_rows = saved
+    ref, _ = _dense_textbook_vec(q, K, V, n, n, 1.0e6)
+    assert np.abs(out - ref).max() > 100 * 1e-6
 
 
 # ------------------------------------------------------------------ closed forms
@@ -673,3 +718,48 @@ def test_identical_heads_select_alone_as_together():
             assert alone[(0, j, g)].sel == grp[(0, j, 0)].sel
             np.testing.assert_allclose(alone[(0, j, g)].out[0], grp[(0, j, 0)].out[g], rtol=0, atol=1e-9)
         np.testing.assert_array_equal(same[(0, j, 0)].out, grp[(0, j, 0)].out)
+
+
+# ------------------------------------------------------------------ forced-selection replay
+
+@pytest.mark.parametrize("seed", range(16))
+def test_replay_with_imposed_sets_matches_brute_force(seed):
+    """The oracle with a level's kept set imposed (the replay used after a near-tie split) equals
+    the float64 brute force with the same set imposed: the levels below, the entries and the
+    outputs. The imposed set is the lowest-scoring s candidates, so it differs from the natural
+    choice."""
+    f, d, G, theta, self_in, n, k, K, V, q, W = _brute_case(seed + 100)
+    tree = build_slice(K, V, W, f, "f32", n_new=n)
+    r = attend_unit(q, K, V, tree, n, f, k, "f32", theta, self_in=self_in)
+    lv = next((lv for lv in sorted(r.scores, reverse=True) if 0 < len(r.sel[lv]) < len(r.scores[lv][0])), None)
+    if lv is None:
+        pytest.skip("no level selects a strict subset")
+    cand, S = r.scores[lv]
+    s = len(r.sel[lv])
+    worst = sorted(int(c) for c in cand[np.lexsort((-np.arange(len(S)), S))][:s])
+    assert worst != r.sel[lv]
+    fixed = {lv: worst}
+    rr = attend_unit(q, K, V, tree, n, f, k, "f32", theta, self_in=self_in, fixed_sel=fixed)
+    b = brute_unit(q, K, V, W, n, f, k, theta, self_in=self_in, fixed_sel=fixed)
+    assert rr.sel[lv] == worst
+    for l2 in range(lv - 1, 0, -1):
+        if rr.flags.get(l2) or b["gap"].get(l2, 1.0) < 1e-5:
+            pytest.skip(f"near tie at level {l2}")
+        assert rr.sel[l2] == b["sel"][l2], l2
+    assert sorted(rr.entries) == sorted(b["entries"])
+    np.testing.assert_allclose(rr.out, b["out"], rtol=0, atol=1e-6)
+    np.testing.assert_allclose(rr.lse, b["lse"], rtol=0, atol=1e-6)
+
+
+def test_replay_rejects_an_invalid_set():
+    rng = np.random.default_rng(1)
+    f, d, G, theta, n, k = 16, 16, 4, 1.0e6, 4096, [2, 2, 2, 2]
+    K, V, q = _rand(rng, (n, d)), _rand(rng, (n, d)), _rand(rng, (G, d))
+    W = np.eye(d, dtype=np.float32)
+    tree = build_slice(K, V, W, f, "f32", n_new=n)
+    r = attend_unit(q, K, V, tree, n, f, k, "f32", theta)
+    assert len(r.sel[2]) == 2
+    with pytest.raises(ValueError):                                   # too few
+        attend_unit(q, K, V, tree, n, f, k, "f32", theta, fixed_sel={2: r.sel[2][:1]})
+    with pytest.raises(ValueError):                                   # not a candidate
+        attend_unit(q, K, V, tree, n, f, k, "f32", theta, fixed_sel={2: [r.sel[2][0], 10 ** 6]})
