@@ -145,6 +145,21 @@ int32_t recsa_decode(const recsa_shape_t* shape, const void* q, int64_t n_q,
                      float* out, float* lse, int32_t* sel, int32_t sel_width,
                      void* workspace, int64_t ws_bytes, void* stream);
 
+/* recsa_decode for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that must not allocate, harnesses that forbid it): the same arguments minus the
+ * workspace, the same kernels and results. The RoPE table goes to a scratch array the library
+ * holds on each GPU (4 MiB, kept until the process ends), so no allocation happens in the call.
+ * Calls on one GPU share that array: calls that overlap in time on one GPU (several streams or
+ * threads) race and must be serialised by the caller. Calls whose table would exceed the array
+ * (about 8K candidate positions at d = 128, e.g. a call that keeps every token of a long prefix)
+ * are rejected with RECSA_ERR_UNSUPPORTED before any launch.
+ * Errors: as recsa_decode, and UNSUPPORTED as above; HIP when the array's address cannot be
+ * looked up. */
+int32_t recsa_decode_noalloc(const recsa_shape_t* shape, const void* q, int64_t n_q,
+                             const void* K, const void* V, const void* tree, int64_t n_tokens,
+                             const int32_t* k_per_level, int32_t n_levels,
+                             float* out, float* lse, int32_t* sel, int32_t sel_width, void* stream);
+
 /* Steps 2-4 for causal prefill [Abstract]: query j sits at position t = q_start + j and sees
  * tokens 0..t, its own token included, through the nodes complete at t + 1 (the tree must hold
  * every node complete at q_start + n_q; nodes beyond a query's prefix are ignored). The result

@@ -416,6 +416,33 @@ int32_t recsa_decode(const recsa_shape_t* shape, const void* q, int64_t n_q, con
                     ws_bytes, stream);
 }
 
+int32_t recsa_decode_noalloc(const recsa_shape_t* shape, const void* q, int64_t n_q, const void* K, const void* V,
+                             const void* tree, int64_t n_tokens, const int32_t* k, int32_t n_levels, float* out,
+                             float* lse, int32_t* sel, int32_t sel_width, void* stream) {
+  // size check first: the scratch holds what recsa_decode's workspace would
+  Info I;
+  int32_t rc = check_shape(shape, &I);
+  if (rc) return rc;
+  if (n_tokens < 0) return fail(RECSA_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (n_tokens > I.cap)
+    return fail(RECSA_ERR_CAPACITY, "%lld tokens exceed the capacity %lld", (long long)n_tokens, (long long)I.cap);
+  rc = check_k(k, n_levels, levels_of(n_tokens, I.f));
+  if (rc) return rc;
+  const int64_t need = table_bytes(I, bounds_for(I, n_tokens, k).P);
+  const int64_t have = static_cast<int64_t>(recsa::kNoallocScratchBytes);
+  if (need > have)
+    return fail(RECSA_ERR_UNSUPPORTED,
+                "this call needs %lld bytes of scratch; the allocation-free entry point has %lld (use recsa_decode "
+                "with a workspace)", (long long)need, (long long)have);
+  void* scratch = nullptr;
+  if (n_q > 0) {
+    hipError_t e = recsa::noalloc_scratch_address(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "scratch address");
+  }
+  return run_attend(shape, q, n_q, K, V, tree, n_tokens, 0, false, k, n_levels, out, lse, sel, sel_width, scratch,
+                    have, stream);
+}
+
 int32_t recsa_prefill(const recsa_shape_t* shape, const void* q, int64_t q_start, int64_t n_q, const void* K,
                       const void* V, const void* tree, const int32_t* k, int32_t n_levels, float* out, float* lse,
                       int32_t* sel, int32_t sel_width, void* workspace, int64_t ws_bytes, void* stream) {

@@ -266,4 +266,9 @@ hipError_t launch_ts_score(const TsArgs& a, int d, bool bf16, int G, hipStream_t
 hipError_t launch_ts_merge(const TsArgs& a, hipStream_t s);
 hipError_t launch_ts_tokens(const TsArgs& a, int d, bool bf16, int G, size_t lds, int64_t B, hipStream_t s);
 
+// ---------------------------------------------------------------- allocation-free decode
+// Device address of the library's scratch array (kNoallocScratchBytes) on the current device
+// (looked up once per device).
+hipError_t noalloc_scratch_address(void** out);
+
 }  // namespace recsa

@@ -59,4 +59,8 @@ __host__ __device__ inline int distill_loss_blocks(int64_t n) {
 // Query rows per workgroup of the dense kernel: 4 waves of 32 (query, head) rows.
 __host__ __device__ inline int dense_queries_per_block(int G) { return 4 * (32 / G); }
 
+// ---------------------------------------------------------------- allocation-free decode
+// Bytes of the library's per-device scratch array: the RoPE table for up to 8191 positions at d = 128.
+constexpr size_t kNoallocScratchBytes = size_t(4) << 20;
+
 }  // namespace recsa

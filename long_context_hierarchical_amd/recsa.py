@@ -25,6 +25,7 @@ EXPORTS = (
     "recsa_distill_step",
     "recsa_dense_workspace_bytes", "recsa_dense_ref_attn", "recsa_rotate_keys",
     "recsa_two_stage_workspace_bytes", "recsa_two_stage_decode", "recsa_two_stage_rotate_blocks",
+    "recsa_decode_noalloc",
 )
 RECSA_DENSE_CAUSAL, RECSA_DENSE_KEYS_ROTATED = 1, 2
 
@@ -90,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "recsa_build_tree": (I32, [SP, P, P, P, I64, I64, P, P]),
             "recsa_decode": (I32, [SP, P, I64, P, P, P, I64, K, I32, P, P, P, I32, P, I64, P]),
             "recsa_prefill": (I32, [SP, P, I64, I64, P, P, P, K, I32, P, P, P, I32, P, I64, P]),
+            "recsa_decode_noalloc": (I32, [SP, P, I64, P, P, P, I64, K, I32, P, P, P, I32, P]),
             "recsa_decode_step": (I32, [SP, P, P, P, P, P, P, P, I64, K, I32, P, P, P, I32, P, I64, P]),
             "recsa_backward_workspace_bytes": (I64, [SP, I64, K, I32]),
             "recsa_distill_workspace_bytes": (I64, [SP, I64, I64, K, I32]),
@@ -188,6 +190,13 @@ def recsa_decode(shape: Shape, q, K, V, tree, n_tokens: int, k_levels, out, lse=
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().recsa_decode(ctypes.byref(shape.c()), _p(q), n_q, _p(K), _p(V), _p(tree), n_tokens, k, nl,
                               _p(out), _p(lse), _p(sel), sel_width, _p(workspace), ws_bytes, _stream(stream)))
+
+
+def recsa_decode_noalloc(shape: Shape, q, K, V, tree, n_tokens: int, k_levels, out, lse=None, sel=None,
+                         sel_width: int = 0, stream=None):
+    k, nl = _k(k_levels)
+    _check(lib().recsa_decode_noalloc(ctypes.byref(shape.c()), _p(q), q.shape[1], _p(K), _p(V), _p(tree), n_tokens,
+                                      k, nl, _p(out), _p(lse), _p(sel), sel_width, _stream(stream)))
 
 
 def recsa_prefill(shape: Shape, q, q_start: int, K, V, tree, k_levels, out, lse=None, sel=None,

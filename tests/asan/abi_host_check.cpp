@@ -66,6 +66,9 @@ int main() {
                                                  static_cast<float*>(fake(5)), nullptr, static_cast<int32_t*>(fake(7)),
                                                  pw > 0 ? pw : 1, fake(8), ws > 0 ? ws : 16, nullptr);
                 expect(rp == RECSA_OK || rp == RECSA_ERR_UNSUPPORTED, "prefill", rp);
+                const int32_t rn = recsa_decode_noalloc(&sh, fake(1), 2, fake(2), fake(3), fake(4), n, k.data(), nl,
+                                                        static_cast<float*>(fake(5)), nullptr, nullptr, 0, nullptr);
+                expect(rn == RECSA_OK || rn == RECSA_ERR_UNSUPPORTED, "decode_noalloc", rn);
                 if (n < cap) {
                   const int32_t sw = recsa_sel_width(&sh, n + 1, n + 1, k.data(), nl);
                   const int64_t sws = recsa_workspace_bytes(&sh, n + 1, k.data(), nl);

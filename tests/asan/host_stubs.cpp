@@ -37,4 +37,10 @@ hipError_t launch_ts_score(const TsArgs&, int, bool, int, hipStream_t) { return 
 hipError_t launch_ts_merge(const TsArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_ts_tokens(const TsArgs&, int, bool, int, size_t, int64_t, hipStream_t) { return hipSuccess; }
 
+alignas(256) static unsigned char fake_scratch[256];
+hipError_t noalloc_scratch_address(void** out) {
+  *out = fake_scratch;
+  return hipSuccess;
+}
+
 }  // namespace recsa
