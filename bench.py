@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-library-legs", action="store_true",
                     help="skip the library flash-attention comparison (torch scaled_dot_product_attention)")
     ap.add_argument("--no-legs", action="store_true", help="skip the dense and prefill comparison legs")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="in the comparison legs, skip the dense comparator (RecSA prefill legs only)")
+    ap.add_argument("--no-prefill64k", action="store_true", help="skip the 64K chunked-prefill workload")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the gradients")
     ap.add_argument("--no-two-stage", action="store_true", help="skip the two-stage block-then-token variant")
     ap.add_argument("--ts-blocks", type=int, default=128, help="two-stage variant: blocks kept")
@@ -388,7 +391,7 @@ def prefill_counts(L, f, k):
     return scored, entries
 
 
-def prefill_64k_leg(R, dev, timed, probe=None):
+def prefill_64k_leg(R, dev, timed, dense=True):
     """The 64K chunked-prefill workload: one sequence, 8 KV heads, bf16, f = 16, k = 8, queries at
     every position in chunks of 4096; per chunk the tree is extended over the chunk's complete
     blocks, then the chunk's queries attend. Timed over all 16 chunks (builds included), next to
@@ -430,13 +433,15 @@ def prefill_64k_leg(R, dev, timed, probe=None):
            "mfma_first_scored_level": {"flops": 2.0 * w.d * w.Hq * mf_rows,
                                        "achieved_over_call": round(2.0 * w.d * w.Hq * mf_rows / (ms * 1e-3) / 1e12, 3),
                                        "unit": "TFLOP/s"}}
-    mode = R.RECSA_DENSE_CAUSAL
-    dws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, w.L, mode), 16), dtype=torch.uint8, device=dev)
-    dms = timed(lambda: R.recsa_dense_ref_attn(sh, q, 0, K, V, w.L, mode, out, None, dws), 1)
-    leg["dense_ms"] = round(dms, 3)
-    leg["dense_tokens_per_s"] = round(w.L / (dms * 1e-3), 1)
-    leg["speedup_vs_dense"] = round(dms / ms, 2)
-    del K, V, q, tree, ws, out, dws
+    if dense:
+        mode = R.RECSA_DENSE_CAUSAL
+        dws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, w.L, mode), 16), dtype=torch.uint8, device=dev)
+        dms = timed(lambda: R.recsa_dense_ref_attn(sh, q, 0, K, V, w.L, mode, out, None, dws), 1)
+        leg["dense_ms"] = round(dms, 3)
+        leg["dense_tokens_per_s"] = round(w.L / (dms * 1e-3), 1)
+        leg["speedup_vs_dense"] = round(dms / ms, 2)
+        del dws
+    del K, V, q, tree, ws, out
     torch.cuda.empty_cache()
     return leg
 
@@ -825,19 +830,22 @@ def main():
         Kr = torch.empty_like(K)
         R.recsa_rotate_keys(sh, K, w.L, Kr)
         mode = R.RECSA_DENSE_KEYS_ROTATED
-        dws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, w.n_queries, mode), 16), dtype=torch.uint8,
-                          device=dev)
-        dout = torch.empty_like(out)
-        ms = timed(lambda: R.recsa_dense_ref_attn(sh, q, 0, Kr, V, w.L, mode, dout, None, dws), 3)
-        legs["dense_decode_batched"] = {"ms_per_call": round(ms, 4), "queries_per_call": n_queries,
-                                        "queries_per_s": round(n_queries / (ms * 1e-3), 1)}
-        q1 = q[:, :1].contiguous()
-        o1 = torch.empty(w.B, 1, w.Hq, w.d, dtype=torch.float32, device=dev)
-        dws1 = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, 1, mode), 16), dtype=torch.uint8, device=dev)
-        ms = timed(lambda: R.recsa_dense_ref_attn(sh, q1, 0, Kr, V, w.L, mode, o1, None, dws1), 10)
-        legs["dense_decode_step"] = {"ms_per_call": round(ms, 4), "queries_per_call": w.B,
-                                     "queries_per_s": round(w.B / (ms * 1e-3), 1),
-                                     "GBps": round(2 * w.B * w.Hkv * w.L * w.d * w.elem_bytes / (ms * 1e-3) / 1e9, 1)}
+        if not args.no_dense:
+            dws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, w.n_queries, mode), 16), dtype=torch.uint8,
+                              device=dev)
+            dout = torch.empty_like(out)
+            ms = timed(lambda: R.recsa_dense_ref_attn(sh, q, 0, Kr, V, w.L, mode, dout, None, dws), 3)
+            legs["dense_decode_batched"] = {"ms_per_call": round(ms, 4), "queries_per_call": n_queries,
+                                            "queries_per_s": round(n_queries / (ms * 1e-3), 1)}
+            q1 = q[:, :1].contiguous()
+            o1 = torch.empty(w.B, 1, w.Hq, w.d, dtype=torch.float32, device=dev)
+            dws1 = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, 1, mode), 16), dtype=torch.uint8,
+                               device=dev)
+            ms = timed(lambda: R.recsa_dense_ref_attn(sh, q1, 0, Kr, V, w.L, mode, o1, None, dws1), 10)
+            legs["dense_decode_step"] = {"ms_per_call": round(ms, 4), "queries_per_call": w.B,
+                                         "queries_per_s": round(w.B / (ms * 1e-3), 1),
+                                         "GBps": round(2 * w.B * w.Hkv * w.L * w.d * w.elem_bytes / (ms * 1e-3) / 1e9,
+                                                       1)}
         # causal prefill of the last chunk of positions [L - c, L): RecSA over the built tree, dense over all keys
         from synthetic import with_overrides
         c = args.prefill_chunk
@@ -860,6 +868,10 @@ def main():
         R.recsa_prefill(sh, qp, w.L - c, K, V, tree, k, pout, None, psel, psw, pws)
         legs["recsa_prefill_last_chunk"]["tile_sharing"] = tile_sharing(psel.cpu().numpy())
         del psel
+        if args.no_dense:
+            del Kr
+            res["breakdown"]["legs"] = legs
+    if not args.no_legs and not args.no_dense:
         pmode = R.RECSA_DENSE_KEYS_ROTATED | R.RECSA_DENSE_CAUSAL
         dpws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, c, pmode), 16), dtype=torch.uint8, device=dev)
         ms = timed(lambda: R.recsa_dense_ref_attn(sh, qp, w.L - c, Kr, V, w.L, pmode, pout, None, dpws), 2)
@@ -1051,9 +1063,9 @@ def main():
         torch.cuda.synchronize()
         res["breakdown"]["calib_copy_bytes"] = 1 << 30
 
-    if not args.no_legs:
+    if not args.no_prefill64k:
         log("64K chunked prefill workload")
-        res["breakdown"]["prefill_64k"] = prefill_64k_leg(R, dev, timed)
+        res["breakdown"]["prefill_64k"] = prefill_64k_leg(R, dev, timed, dense=not args.no_dense)
         if cpu is not None:
             res["breakdown"]["prefill_64k"]["cpu_oracle_tokens_per_s"] = round(cpu["prefill_64k"]["tokens_per_s"], 2)
 

@@ -413,7 +413,7 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
   float* bc = reinterpret_cast<float*>(lds + L.bc);   // wave 0 -> all: alpha[G], l[G]
   int32_t* info = reinterpret_cast<int32_t*>(lds + L.info);
   uint4* vst = reinterpret_cast<uint4*>(lds_all + slots * L.total);   // staged value rows (several waves)
-  uint16_t* mstage = reinterpret_cast<uint16_t*>(lds_all + slots * L.total);   // matrix-core rows (same region)
+  uint16_t* mstage = reinterpret_cast<uint16_t*>(lds_all + slots * L.total + (NW > 1 ? a.stage_bytes : 0));
   const bool staged = NW > 1 && a.pv_stage == 1;          // rounds of SR rows
   const bool prefetched = NW > 1 && a.pv_stage == 2;      // a chunk's rows, loaded while it is scored
   // the G logits (then weights) of candidate r: one vector LDS access
@@ -499,10 +499,32 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
       break;
     }
   }
+  // several waves, prefetch mode: the value rows of candidates [0, cn) -- rounded up to whole
+  // 8-row residue steps with copies of the last row -- go straight from memory to LDS
+  // (row-major, D * ESZ bytes a row) while the chunk is scored and selected
+  auto prefetch_values = [&](const void* vsrc, int64_t rowbase, int32_t cn) {
+    const int32_t pieces = ((cn + 8 * RPP - 1) / (8 * RPP)) * (8 * RPP) * SCPR;
+    for (int32_t jw = wid; jw * kWave < pieces; jw += NW) {
+      const int32_t idx = jw * kWave + lane;
+      const int32_t r = idx / SCPR;
+      const int64_t row = rowbase + cid[r < cn ? r : cn - 1];
+      const char* g = static_cast<const char*>(vsrc) + row * (D * ESZ) + (idx % SCPR) * 16;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
+                                       (__attribute__((address_space(3))) void*)(vst + jw * kWave), 16, 0, 0);
+    }
+  };
   if constexpr (MF) {
     if (tid == 0) {
       info[0] = ls;
       info[1] = cs;
+    }
+    // several waves: the first scored level's candidates are its nodes in order, so their value
+    // rows can be requested now, before the tile is computed (as score_rows does for a level it
+    // scores)
+    if (prefetched && active && ls > 0) {
+      for (int32_t r = tid; r < cs; r += NT) cid[r] = r;
+      bsync();
+      prefetch_values(a.tree.NV[ls], bh * a.tree.rows[ls], cs);
     }
     __syncthreads();
     mf_shared_levels<D, G>(a, lds_all, L, slots, slot, ls, cs, qs, mstage, bh, tid, NT);
@@ -580,20 +602,6 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
     bsync();
   };
 
-  // several waves, prefetch mode: the value rows of candidates [0, cn) -- rounded up to whole
-  // 8-row residue steps with copies of the last row -- go straight from memory to LDS
-  // (row-major, D * ESZ bytes a row) while the chunk is scored and selected
-  auto prefetch_values = [&](const void* vsrc, int64_t rowbase, int32_t cn) {
-    const int32_t pieces = ((cn + 8 * RPP - 1) / (8 * RPP)) * (8 * RPP) * SCPR;
-    for (int32_t jw = wid; jw * kWave < pieces; jw += NW) {
-      const int32_t idx = jw * kWave + lane;
-      const int32_t r = idx / SCPR;
-      const int64_t row = rowbase + cid[r < cn ? r : cn - 1];
-      const char* g = static_cast<const char*>(vsrc) + row * (D * ESZ) + (idx % SCPR) * 16;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
-                                       (__attribute__((address_space(3))) void*)(vst + jw * kWave), 16, 0, 0);
-    }
-  };
   // logits of candidates [c0, c0 + cn) (index = RoPE position) -> zs[r * G + hh], sc[r].
   // Two row buffers alternate: the rows of the next pass are requested after this pass's
   // RoPE-table entries, so waiting for the table does not wait for them. The loop body has
@@ -727,7 +735,8 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
       sc[r] = S;
     }
     bsync();
-    if (prefetched) prefetch_values(vsrc, rowbase, cn);
+    (void)vsrc;
+    (void)rowbase;   // several waves: its value rows were requested before the tile
   };
   // qpos >= 0: rotate the query heads at qpos first (a level's first chunk)
   auto score_rows = [&](const void* src, const void* vsrc, int64_t rowbase, const CandMap& cm, int32_t c0, int32_t cn,
@@ -1129,18 +1138,20 @@ static hipError_t launch_attend_t(const AttnArgs& a, size_t lds, int64_t B, hipS
     constexpr size_t kStage = 4 * kWave * 4 * 16;
     hipError_t e = allow_full_lds<D, BF16, G, 4>();
     if (e != hipSuccess) return e;
-    // the staged value rows and the tile's rows share one region (the tile is done first)
-    if (lds + std::max(kFull, mf) <= 65536) {
-      AttnArgs b = a;
+    // the staged value rows, then the tile's rows (the first scored level's value rows are
+    // requested before its tile is computed)
+    AttnArgs b = a;
+    if (lds + kFull + mf <= kLdsMax) {
       b.pv_stage = 2;
-      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + std::max(kFull, mf), s, b);
-    } else if (lds + std::max(kStage, mf) <= 65536) {
-      AttnArgs b = a;
+      b.stage_bytes = static_cast<int32_t>(kFull);
+    } else if (lds + kStage + mf <= kLdsMax) {
       b.pv_stage = 1;
-      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + std::max(kStage, mf), s, b);
+      b.stage_bytes = static_cast<int32_t>(kStage);
     } else {
-      hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + mf, s, a);
+      b.pv_stage = 0;
+      b.stage_bytes = 0;
     }
+    hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + b.stage_bytes + mf, s, b);
   } else {
     // bf16: up to 8 units of one KV head per workgroup, one wave each, whose rows fill the 32
     // rows of the first scored level's tile, as many as LDS holds; float32: one unit

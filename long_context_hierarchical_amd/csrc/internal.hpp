@@ -98,6 +98,8 @@ struct AttnArgs {
   int32_t zcap;         // capacity of a scored candidate list (selecting levels and token-level chunks)
   int32_t pv_stage;     // set by the launcher, several waves per unit: value rows through LDS in
                         // rounds (1) or prefetched for a whole chunk while it is scored (2)
+  int32_t stage_bytes;  // set by the launcher: LDS bytes of that value staging (the matrix-core
+                        // tile's rows follow it)
   LevelK k;
   TreeLevels tree;
 };

@@ -52,12 +52,16 @@ def _slim(r):
 
 
 class Slim:
-    """Attribute view of a slimmed unit result, as compare_unit expects."""
+    """Attribute view of a slimmed unit result (RecSA: as compare_unit expects; two-stage: blocks,
+    tokens, flags, out, lse and z, as the two-stage comparison expects)."""
 
     def __init__(self, d):
-        self.sel, self.flags, self.out, self.lse = d["sel"], d["flags"], d["out"], d["lse"]
+        self.flags, self.out, self.lse = d["flags"], d["out"], d["lse"]
         self.z = True if d["has_entries"] else None
-        self.n_entries, self.zmax, self.scores = d["n_entries"], d["zmax"], d["scores"]
+        if "blocks" in d:
+            self.blocks, self.tokens = d["blocks"], d["tokens"]
+        else:
+            self.sel, self.n_entries, self.zmax, self.scores = d["sel"], d["n_entries"], d["zmax"], d["scores"]
 
 
 def _slice_job(job):
@@ -73,7 +77,7 @@ def _slice_job(job):
         out = {"slice": (b, h)}
         if job.get("return_kv"):
             out["K"], out["V"] = K, V
-        if not job.get("units") and not job.get("digest"):
+        if not job.get("units") and not job.get("digest") and not job.get("ts_units"):
             return out
         Kf, Vf = oracle.from_storage(K, w.dtype), oracle.from_storage(V, w.dtype)
         Wf = oracle.from_storage(gen_W(w), w.dtype)
@@ -82,7 +86,7 @@ def _slice_job(job):
             out["digest"] = [(level_digest(oracle.to_storage(NK, w.dtype)), level_digest(oracle.to_storage(NV, w.dtype)))
                              for NK, NV in tree]
         G = w.G
-        k = job["k"]
+        k = job.get("k")
         res = {}
         for (j, n, self_in, fixed) in job.get("units", []):
             qg = oracle.from_storage(q[j, h * G:(h + 1) * G], w.dtype)
@@ -90,6 +94,15 @@ def _slice_job(job):
                                    fixed_sel=fixed)
             res[(j, n, self_in, tuple(sorted((lv, tuple(v)) for lv, v in (fixed or {}).items())))] = _slim(r)
         out["units"] = res
+        if job.get("ts_units"):
+            from oracle.two_stage import two_stage_unit
+            ts = {}
+            for (j, kb, kt) in job["ts_units"]:
+                qg = oracle.from_storage(q[j, h * G:(h + 1) * G], w.dtype)
+                r = two_stage_unit(qg, Kf, Vf, tree[0][0], w.L, w.f, kb, kt, w.dtype, w.theta)
+                ts[(j, kb, kt)] = {"blocks": r.blocks, "tokens": r.tokens, "flags": r.flags, "out": r.out,
+                                   "lse": r.lse, "has_entries": r.z is not None}
+            out["ts_units"] = ts
         return out
 
 

@@ -169,24 +169,26 @@ def test_two_stage_rotated_block_cache():
         assert np.array_equal(storage_bits(bk[0, h]), oracle.to_storage(want, w.dtype)), h
 
 
-def test_two_stage_full_size_524k():
-    """The 524K workload's shape (4 sequences x 524,288 tokens, 8 KV heads, 32 query heads, d = 128,
-    bf16, f = 16) with 128 blocks and 512 tokens kept, 256 queries per sequence in one call -- the
-    configuration the benchmark times; the oracle checks the first and last query of every
-    (sequence, KV head)."""
-    w = WORKLOADS["c2"]
-    n_q, kb, kt = 256, 128, 512
+def _full_size(name, n_q, kb, kt, checked_queries):
+    """One workload at full size in the configuration the benchmark times: spawned workers
+    regenerate every (sequence, KV head) slice (uploaded as it arrives), build its level 1 and run
+    the oracle's two-stage selection for the checked queries of that slice."""
+    import oracle_pool as OP
+    w = WORKLOADS[name]
     dev = "cuda:0"
     td = torch.bfloat16
     K = torch.empty(w.B, w.Hkv, w.L, w.d, dtype=td, device=dev)
     V = torch.empty_like(K)
+
+    def up(r):
+        b, h = r["slice"]
+        K[b, h] = torch.from_numpy(r["K"]).view(td).to(dev)
+        V[b, h] = torch.from_numpy(r["V"]).view(td).to(dev)
+        _say(f"two-stage {name}: slice {(b, h)} uploaded, oracle done")
+    jobs = [dict(workload=name, slice=(b, h), n_q=n_q, return_kv=True,
+                 ts_units=[(j, kb, kt) for j in checked_queries]) for b in range(w.B) for h in range(w.Hkv)]
+    res = OP.run_slices(jobs, on_result=up)
     qs = np.stack([gen_queries(w, b, n_q) for b in range(w.B)])
-    for b in range(w.B):
-        for h in range(w.Hkv):
-            Kb, Vb = gen_kv_slice(w, b, h, qs[b])
-            K[b, h] = torch.from_numpy(Kb).view(td).to(dev)
-            V[b, h] = torch.from_numpy(Vb).view(td).to(dev)
-        _say(f"two-stage 524K: sequence {b} uploaded")
     Wn = gen_W(w)
     sh = R.Shape(w.B, w.Hkv, w.Hq, w.d, w.f, w.dtype, w.L, 0.0, w.theta)
     tree = torch.zeros(R.recsa_tree_bytes(sh), dtype=torch.uint8, device=dev)
@@ -196,61 +198,21 @@ def test_two_stage_full_size_524k():
         pass
     g = _G()
     g.w, g.shape, g.dev, g.q, g.K, g.V, g.tree = w, sh, dev, torch.from_numpy(qs).view(td).to(dev), K, V, tree
-    res = _run(g, w.L, kb, kt)
-    _say("two-stage 524K: gpu done")
-    Wf = oracle.from_storage(Wn, w.dtype)
-    G = w.G
-    ref = {}
-    for b in range(w.B):
-        for h in range(w.Hkv):
-            Kb, Vb = gen_kv_slice(w, b, h, qs[b])
-            Kf, Vf = oracle.from_storage(Kb, w.dtype), oracle.from_storage(Vb, w.dtype)
-            NK1 = oracle.build_slice(Kf, Vf, Wf, w.f, w.dtype, n_new=w.L)[0][0]
-            for j in (0, n_q - 1):
-                qg = oracle.from_storage(qs[b, j, h * G:(h + 1) * G], w.dtype)
-                ref[(b, j, h)] = two_stage_unit(qg, Kf, Vf, NK1, w.L, w.f, kb, kt, w.dtype, w.theta)
-        _say(f"two-stage 524K: sequence {b} checked by the oracle")
-    _say(f"two-stage 524K: {_compare(w, res, ref)}")
+    out = _run(g, w.L, kb, kt)
+    _say(f"two-stage {name}: gpu done")
+    ref = {(b, j, h): OP.Slim(r["ts_units"][(j, kb, kt)]) for (b, h), r in res.items() for j in checked_queries}
+    _say(f"two-stage {name}: {_compare(w, out, ref)}")
+
+
+def test_two_stage_full_size_524k():
+    """The 524K workload's shape (4 sequences x 524,288 tokens, 8 KV heads, 32 query heads, d = 128,
+    bf16, f = 16) with 128 blocks and 512 tokens kept, 256 queries per sequence in one call -- the
+    configuration the benchmark times; the oracle checks 8 queries of every (sequence, KV head)."""
+    _full_size("c2", 256, 128, 512, (0, 31, 64, 100, 127, 128, 200, 255))
 
 
 def test_two_stage_full_size_2m():
     """The 2M workload's shape (2,097,152 tokens, 8 KV heads, 32 query heads, d = 128, bf16,
     f = 32): 65,536 blocks per slice, 64 slabs whose lists merge into 8192 candidates per query
-    (more than 64 KB of LDS for the merge); 16 queries, the oracle checks the first and last of
-    every KV head."""
-    w = WORKLOADS["c4"]
-    n_q, kb, kt = 16, 128, 512
-    dev = "cuda:0"
-    td = torch.bfloat16
-    K = torch.empty(w.B, w.Hkv, w.L, w.d, dtype=td, device=dev)
-    V = torch.empty_like(K)
-    qs = np.stack([gen_queries(w, b, n_q) for b in range(w.B)])
-    for h in range(w.Hkv):
-        Kb, Vb = gen_kv_slice(w, 0, h, qs[0])
-        K[0, h] = torch.from_numpy(Kb).view(td).to(dev)
-        V[0, h] = torch.from_numpy(Vb).view(td).to(dev)
-    _say("two-stage 2M: uploaded")
-    Wn = gen_W(w)
-    sh = R.Shape(w.B, w.Hkv, w.Hq, w.d, w.f, w.dtype, w.L, 0.0, w.theta)
-    tree = torch.zeros(R.recsa_tree_bytes(sh), dtype=torch.uint8, device=dev)
-    R.recsa_build_tree(sh, K, V, torch.from_numpy(Wn).view(td).to(dev), 0, w.L, tree)
-
-    class _G:
-        pass
-    g = _G()
-    g.w, g.shape, g.dev, g.q, g.K, g.V, g.tree = w, sh, dev, torch.from_numpy(qs).view(td).to(dev), K, V, tree
-    res = _run(g, w.L, kb, kt)
-    _say("two-stage 2M: gpu done")
-    Wf = oracle.from_storage(Wn, w.dtype)
-    G = w.G
-    ref = {}
-    for h in range(w.Hkv):
-        Kb, Vb = gen_kv_slice(w, 0, h, qs[0])
-        Kf, Vf = oracle.from_storage(Kb, w.dtype), oracle.from_storage(Vb, w.dtype)
-        NK1 = oracle.build_slice(Kf, Vf, Wf, w.f, w.dtype, n_new=w.L)[0][0]
-        for j in (0, n_q - 1):
-            qg = oracle.from_storage(qs[0, j, h * G:(h + 1) * G], w.dtype)
-            ref[(0, j, h)] = two_stage_unit(qg, Kf, Vf, NK1, w.L, w.f, kb, kt, w.dtype, w.theta)
-        _say(f"two-stage 2M: KV head {h} checked by the oracle")
-    _say(f"two-stage 2M: {_compare(w, res, ref)}")
-
+    (more than 64 KB of LDS for the merge); 16 queries, the oracle checks 4 of every KV head."""
+    _full_size("c4", 16, 128, 512, (0, 5, 10, 15))
