@@ -745,8 +745,8 @@ def main():
     build_launches = pool_launches(w)
     kinfo = {
         "pool_kernel": dict(bytes=bb / build_launches, ms=build_ms / build_launches,
-                            src=kernel_hash("build_tree.hip", "common.hpp")),
-        "attend_kernel": dict(bytes=db, ms=decode_ms, src=kernel_hash("attend.hip", "common.hpp", "lanes.hpp"),
+                            src=kernel_hash("build_tree.hip", "common.hpp", "sizing.hpp")),
+        "attend_kernel": dict(bytes=db, ms=decode_ms, src=kernel_hash("attend.hip", "common.hpp", "lanes.hpp", "sizing.hpp"),
                               unique=decode_unique_bytes(w, k, sel.cpu().numpy())),
     }
     dom = "pool_kernel" if build_ms >= decode_ms else "attend_kernel"
