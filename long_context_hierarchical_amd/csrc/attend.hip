@@ -70,6 +70,35 @@ __device__ __forceinline__ void load4(const void* base, int64_t off, float (&x)[
 
 typedef __bf16 mf_bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float mf_f32x16_t __attribute__((ext_vector_type(16)));
+typedef short mv_i16x4_t __attribute__((ext_vector_type(4)));
+typedef short mv_i16x8_t __attribute__((ext_vector_type(8)));
+typedef float mv_f32x4_t __attribute__((ext_vector_type(4)));
+
+// The value pass on the matrix cores (bf16 storage, G >= 2). O[h][c] += sum over 4 candidate rows
+// of P[h][r] V[r][c] is two v_mfma_f32_4x4x4_16b_bf16 per 64 value columns and 4 query heads: their
+// 16 blocks (block b = lane / 4) each take 4 columns and all of them the same 4 x 4 block of
+// weights. Lane l supplies the weights of head l % 4 for the 4 rows (A) and one column of the 64
+// for the same rows (B), and receives O[4 heads][that column] in its 4 accumulators. With one wave
+// a lane loads its columns of each row itself (2 lane and 2 lane + 1 at D = 128, lane at D = 64);
+// with several waves the rows sit in LDS and a transposing read gives lane l column l. A weight p
+// enters as two bf16 terms, hi = bf16(p) and lo = bf16(p - hi) (p - hi is exact in float32), one
+// product each: the weight is held to 2^-17 of itself instead of bf16's 2^-9, and the sums stay
+// float32. The matrix core forms each output element from its row of A and its column of B alone,
+// and every launch shape runs the same sequence of products for an element -- the candidates'
+// 4-row quads in ascending order up to the next multiple of 16 rows (hi, then lo), the rows past
+// the last candidate and the kept ones with weight 0 -- so results do not depend on the launch.
+__device__ __forceinline__ mv_i16x4_t mv_read_tr(const uint16_t* p) {
+  // within each 16 lanes, lane 4j + c addresses row j of 4 at its columns 4c .. 4c + 3 and lane l
+  // receives column l of the 4 rows (gfx950's ds_read_b64_tr_b16)
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) mv_i16x4_t*)(p));
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return static_cast<uint16_t>(__builtin_bit_cast(uint32_t, pack_bf16_rne(x, 0.0f)) & 0xFFFFu);
+}
+
+// orders the surrounding LDS accesses for the compiler (a wave's LDS accesses execute in order)
+__device__ __forceinline__ void lds_order() { __asm__ volatile("" ::: "memory"); }
 
 // Candidate index -> node (or token) id: children of the kept parents, then orphans.
 // Ids and indices fit in 32 bits (the capacity is at most INT32_MAX); a power-of-two
@@ -391,6 +420,10 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
   // bf16 storage: the first level a unit scores holds every node of that level, in order, for
   // every unit of the workgroup; its logits come from one matrix-core tile (see mf_level below)
   constexpr bool MF = BF16;
+  // bf16 storage with G >= 2: the value pass on the matrix cores (mv_read_tr above)
+  constexpr bool MV = BF16 && G >= 2;
+  constexpr int HG = G > 4 ? G / 4 : 1;   // groups of 4 query heads
+  constexpr int CB = D / 64;              // 64-column blocks of the value rows
   extern __shared__ __align__(16) unsigned char lds_all[];
   // NW = 1: a workgroup holds `slots` units, one wave each; NW > 1: one unit on NW waves
   const int slots = NW == 1 && MF ? static_cast<int>(blockDim.x) / kWave : 1;
@@ -416,6 +449,12 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
   uint16_t* mstage = reinterpret_cast<uint16_t*>(lds_all + slots * L.total + (NW > 1 ? a.stage_bytes : 0));
   const bool staged = NW > 1 && a.pv_stage == 1;          // rounds of SR rows
   const bool prefetched = NW > 1 && a.pv_stage == 2;      // a chunk's rows, loaded while it is scored
+  // matrix-core value pass: the softmax weights as bf16 pairs, [row / 4][head][hi, lo][row % 4]
+  // (16 bytes per quad and head, 4 G bytes per row: the size of a row's logits). One wave: in the
+  // unit's logit array (an iteration of the weight pass writes the bytes of the logit rows it has
+  // just read). Several waves: a region of their own after the tile's rows.
+  uint16_t* pw = NW == 1 ? reinterpret_cast<uint16_t*>(zs)
+                         : reinterpret_cast<uint16_t*>(lds_all + slots * L.total + a.stage_bytes + mf_stage_bytes(D));
   // the G logits (then weights) of candidate r: one vector LDS access
   auto zrow_load = [&](int32_t r, float (&z)[G]) {
     if constexpr (G % 4 == 0) {
@@ -444,7 +483,8 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
   };
 
   const int lane = threadIdx.x % kWave;
-  const int wid = NW == 1 ? 0 : static_cast<int>(threadIdx.x) / kWave;   // wave within the unit
+  // wave within the unit (wave-uniform: a scalar register)
+  const int wid = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   const int tid = NW == 1 ? lane : static_cast<int>(threadIdx.x);         // thread within the unit
   constexpr int NT = NW * kWave;
   auto bsync = [&]() {
@@ -544,6 +584,43 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
 #pragma unroll
     for (int e = 0; e < VEW; ++e) acc[hh][e] = 0.0f;
   }
+  // matrix-core value pass: oacc[hg][cb][i] = O[head 4 hg + i][column]: with one wave, column
+  // 2 lane + cb (D = 128) or lane (D = 64); with several waves, column 64 cb + lane
+  mv_f32x4_t oacc[HG][CB];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) oacc[hg][cb] = mv_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // several waves: this lane's 8-byte chunk of a quad's transposed read (row mv_j of the quad,
+  // 16-column block mv_bl, chunk mv_c of it)
+  const int mv_j = (lane & 15) >> 2, mv_c = lane & 3, mv_bl = lane >> 4;
+  // this lane's weight pair (hi, lo) of head group hg for quad qd; heads past G get 0
+  auto mv_weights = [&](int32_t qd, int hg) __attribute__((always_inline)) {
+    const int hd = 4 * hg + (lane & 3);
+    const mv_i16x8_t w = *reinterpret_cast<const mv_i16x8_t*>(pw + (qd * G + (hd < G ? hd : G - 1)) * 8);
+    const mv_i16x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
+    return hd < G ? w : z;
+  };
+  auto mv_mfma = [&](int hg, int cb, const mv_i16x8_t& w, const mv_i16x4_t& bv) __attribute__((always_inline)) {
+    oacc[hg][cb] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_shufflevector(w, w, 0, 1, 2, 3), bv, oacc[hg][cb], 0, 0, 0);
+    oacc[hg][cb] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_shufflevector(w, w, 4, 5, 6, 7), bv, oacc[hg][cb], 0, 0, 0);
+  };
+  // the products of quad qd (rows 4 qd .. 4 qd + 3 of the chunk); bop(cb) is this lane's B
+  // operand of column block cb
+  auto mv_quad = [&](int32_t qd, auto bop) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      const mv_i16x8_t w = mv_weights(qd, hg);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) mv_mfma(hg, cb, w, bop(cb));
+    }
+  };
+  auto mv_weight = [&](int32_t r, int hh, float p) {
+    const uint16_t hi = bf16_bits(p);
+    uint16_t* w = pw + ((r >> 2) * G + hh) * 8 + (r & 3);
+    w[0] = hi;
+    w[4] = bf16_bits(p - __uint_as_float(static_cast<uint32_t>(hi) << 16));
+  };
 
   // rotated query operands for the current level -> qr: lane slot ssub holds the 8
   // rotate-half pairs (elements 8*ssub + e and HALF + 8*ssub + e, e < 8) of every head
@@ -862,8 +939,12 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
         for (int32_t r = lane; r < cn; r += kWave) {
           const bool skip = use_flags && flags[r];
           const float p = skip ? 0.0f : expf(zs[r * G + hh] - mn);
-          zs[r * G + hh] = p;
+          if constexpr (MV) mv_weight(r, hh, p);
+          else zs[r * G + hh] = p;
           ls += p;
+        }
+        if constexpr (MV) {
+          for (int32_t r = cn + lane; r < ((cn + 15) & ~15); r += kWave) mv_weight(r, hh, 0.0f);
         }
         const float lsum = wave_sum_dpp(ls);
         const float alpha = expf(m_run[hh] - mn);
@@ -890,17 +971,32 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
       float ls[G];
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) ls[hh] = 0.0f;
+      // matrix-core value pass: the bf16 weight pairs overwrite the logit array (pw); iteration t
+      // writes the bytes of logit rows [64 t, 64 t + 64), the ones it has read, and lds_order
+      // keeps each iteration's reads before its writes
+      if constexpr (MV) lds_order();
       for (int32_t r = lane; r < cn; r += kWave) {
         const bool skip = use_flags && flags[r];
         float z[G];
         zrow_load(r, z);
+        if constexpr (MV) lds_order();
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
           const float p = skip ? 0.0f : expf(z[hh] - mnew[hh]);
           z[hh] = p;
           ls[hh] += p;
         }
-        zrow_store(r, z);
+        if constexpr (MV) {
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) mv_weight(r, hh, z[hh]);
+        } else {
+          zrow_store(r, z);
+        }
+      }
+      if constexpr (MV) {
+        for (int32_t r = cn + lane; r < ((cn + 15) & ~15); r += kWave)
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) mv_weight(r, hh, 0.0f);
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
@@ -908,8 +1004,13 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
         const float alpha = expf(m_run[hh] - mnew[hh]);
         l_run[hh] = l_run[hh] * alpha + lsum;
         m_run[hh] = mnew[hh];
+        if constexpr (MV) {
 #pragma unroll
-        for (int e = 0; e < VEW; ++e) acc[hh][e] *= alpha;
+          for (int cb = 0; cb < CB; ++cb) oacc[hh / 4][cb][hh % 4] *= alpha;
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEW; ++e) acc[hh][e] *= alpha;
+        }
       }
     }
     bsync();
@@ -918,9 +1019,39 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
       for (int hh = 0; hh < G; ++hh) {
         const float alpha = bc[hh];
         l_run[hh] = bc[G + hh];
+        if constexpr (MV) {
 #pragma unroll
-        for (int e = 0; e < VEW; ++e) acc[hh][e] *= alpha;
+          for (int cb = 0; cb < CB; ++cb) oacc[hh / 4][cb][hh % 4] *= alpha;
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEW; ++e) acc[hh][e] *= alpha;
+        }
       }
+      // matrix-core value pass: the quads of LDS rows [0, sn) (copies of a finite row up to the
+      // next multiple of 16, weight 0), wave w taking (head group, column block) pair w; four
+      // quads' operands are read before their products
+      auto chains_mv = [&](int32_t s0, int32_t sn) {
+        const uint16_t* vs = reinterpret_cast<const uint16_t*>(vst);
+        const int32_t nq = (sn + 15) / 16 * 4;
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            if (hg * CB + cb != wid) continue;
+            const uint16_t* bp = vs + mv_j * D + 64 * cb + 16 * mv_bl + 4 * mv_c;
+            for (int32_t qd = 0; qd < nq; qd += 4) {
+              mv_i16x8_t w[4];
+              mv_i16x4_t bv[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                w[t] = mv_weights((s0 >> 2) + qd + t, hg);
+                bv[t] = mv_read_tr(bp + (qd + t) * 4 * D);
+              }
+#pragma unroll
+              for (int t = 0; t < 4; ++t) mv_mfma(hg, cb, w[t], bv[t]);
+            }
+          }
+      };
       // 8 rows of the residue per step from LDS rows [0, sn) of vst (rows up to the next
       // multiple of 8 * RPP hold finite copies), their reads issued together and no branch: a
       // kept row has weight 0 and a row past the end gets weight 0, and fmaf(0, v, acc)
@@ -954,7 +1085,8 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
         }
       };
       if (prefetched) {
-        chains(0, cn);
+        if constexpr (MV) chains_mv(0, cn);
+        else chains(0, cn);
         bsync();
         return;
       }
@@ -969,7 +1101,8 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
           vst[tid + 3 * NT] = st3;
           if (s0 + SR < cn) stage_issue(s0 + SR);
           bsync();
-          chains(s0, cn - s0 < SR ? cn - s0 : SR);
+          if constexpr (MV) chains_mv(s0, cn - s0 < SR ? cn - s0 : SR);
+          else chains(s0, cn - s0 < SR ? cn - s0 : SR);
           bsync();
         }
         return;
@@ -978,6 +1111,51 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
     // value rows: two buffers alternate, the next iteration's rows are requested before this
     // iteration's are accumulated; every row slot loads (a kept or absent row loads a valid
     // row and adds nothing), so no load sits behind a branch
+    if constexpr (MV && NW == 1) {
+      // matrix-core value pass with one wave: every lane loads its columns of every row -- 4
+      // bytes, columns 2 lane and 2 lane + 1 (D = 128; column block cb = the column's parity), or
+      // 2 bytes, column lane (D = 64) -- so that a quad's 4 rows at one column pack straight into
+      // the B operand. 8 rows (2 quads) per group; the next group's rows are in flight while this
+      // group's products run. Rows past the last candidate load the last candidate's row; their
+      // weights are 0 (padded to a multiple of 16 rows), like the kept rows'.
+      using RT = typename std::conditional<D == 128, uint32_t, uint16_t>::type;
+      static_assert(D * 2 == 64 * static_cast<int>(sizeof(RT)), "a row is 64 units of RT");
+      const RT* vb = static_cast<const RT*>(vsrc) + rowbase * 64 + lane;
+      auto gfetch = [&](int32_t r0, RT (&raw)[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int32_t r = r0 + e;
+          raw[e] = vb[static_cast<int64_t>(cid[r < cn ? r : cn - 1]) * 64];
+        }
+      };
+      auto gcompute = [&](int32_t r0, const RT (&raw)[8]) {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          uint32_t w[CB][2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const uint32_t x = raw[4 * qq + 2 * t], y = raw[4 * qq + 2 * t + 1];
+            if constexpr (D == 128) {
+              w[0][t] = (x & 0xFFFFu) | (y << 16);
+              w[CB - 1][t] = (x >> 16) | (y & 0xFFFF0000u);
+            } else {
+              w[0][t] = x | (y << 16);
+            }
+          }
+          mv_quad((r0 >> 2) + qq, [&](int cb) { return __builtin_bit_cast(mv_i16x4_t, make_uint2(w[cb][0], w[cb][1])); });
+        }
+      };
+      RT ra[8], rb[8];
+      gfetch(0, ra);
+      for (int32_t r0 = 0; r0 < cn; r0 += 16) {
+        gfetch(r0 + 8, rb);
+        gcompute(r0, ra);
+        gfetch(r0 + 16, ra);
+        gcompute(r0 + 8, rb);
+      }
+      bsync();
+      return;
+    }
     auto vfetch = [&](int32_t r0, RawV<BF16, VEW> (&raw)[PV_UNROLL]) {
 #pragma unroll
       for (int u = 0; u < PV_UNROLL; ++u) {
@@ -1064,14 +1242,36 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
   }
 
   // --- merge the row groups' partial sums, normalise, write ---------------------------
+  const int64_t obase = ((b * a.n_q + j) * a.Hq + static_cast<int64_t>(h) * G) * D;
+  if constexpr (MV) {
+    // head 4 hg + i of oacc[hg][cb] (with several waves, of this wave's pair hg * CB + cb)
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hd = 4 * hg + i;
+        if (hd >= G) continue;
+        const float l = l_run[hd];
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        float* o = a.out + obase + hd * D;
+        if constexpr (NW == 1 && D == 128) {
+          *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(oacc[hg][0][i] * inv, oacc[hg][1][i] * inv);
+        } else if constexpr (NW == 1) {
+          o[lane] = oacc[hg][0][i] * inv;
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            if (hg * CB + cb == wid) o[64 * cb + lane] = oacc[hg][cb][i] * inv;
+        }
+      }
+  }
 #pragma unroll
   for (int off = RL; off < kWave; off <<= 1)
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
       for (int e = 0; e < VEW; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], off);
-  const int64_t obase = ((b * a.n_q + j) * a.Hq + static_cast<int64_t>(h) * G) * D;
-  if (rg == 0) {
+  if (!MV && rg == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const float l = l_run[hh];
@@ -1140,18 +1340,23 @@ static hipError_t launch_attend_t(const AttnArgs& a, size_t lds, int64_t B, hipS
     if (e != hipSuccess) return e;
     // the staged value rows, then the tile's rows (the first scored level's value rows are
     // requested before its tile is computed)
+    // bf16 with G >= 2: then the bf16 weights of the matrix-core value pass, which reads the
+    // value rows from LDS (a staging mode is always granted: a unit's LDS is at most 64 KB)
+    constexpr bool kMV = BF16 && G >= 2;
+    const size_t pwb = kMV ? static_cast<size_t>(4 * G) * static_cast<size_t>(a.zcap) : 0;
     AttnArgs b = a;
-    if (lds + kFull + mf <= kLdsMax) {
+    if (lds + kFull + mf + pwb <= kLdsMax) {
       b.pv_stage = 2;
       b.stage_bytes = static_cast<int32_t>(kFull);
-    } else if (lds + kStage + mf <= kLdsMax) {
+    } else if (lds + kStage + mf + pwb <= kLdsMax) {
       b.pv_stage = 1;
       b.stage_bytes = static_cast<int32_t>(kStage);
     } else {
+      if (kMV) return hipErrorInvalidValue;
       b.pv_stage = 0;
       b.stage_bytes = 0;
     }
-    hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + b.stage_bytes + mf, s, b);
+    hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + b.stage_bytes + mf + pwb, s, b);
   } else {
     // bf16: up to 8 units of one KV head per workgroup, one wave each, whose rows fill the 32
     // rows of the first scored level's tile, as many as LDS holds; float32: one unit
