@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "librecsa.so")
 SOURCES = ["build_tree.hip", "step.hip", "attend.hip", "backward.hip", "distill.hip", "dense.hip", "two_stage.hip",
-           "noalloc.hip", "api.cpp"]
+           "noalloc.hip", "rope_cache.hip", "api.cpp"]
 # HBM read/copy probe (a separate program, not part of the library): the achievable bandwidth
 PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
 PROBE = os.path.join(PKG, "probe", "hbm_probe")

@@ -186,13 +186,27 @@ int64_t table_bytes(const Info& I, int64_t P) {
   return ((P + 1) * (I.d / 2) * static_cast<int64_t>(sizeof(float2)) + kTableAlign - 1) / kTableAlign * kTableAlign;
 }
 
-int32_t fill_table(const Info& I, int64_t P, void* ws, hipStream_t st) {
-  if (I.theta == 0.0f) return RECSA_OK;
+recsa::InvFreq inv_freq_of(const Info& I) {
   recsa::InvFreq iv{};
   for (int i = 0; i < I.d / 2; ++i)
     iv.w[i] = static_cast<float>(std::pow(static_cast<double>(I.theta), -2.0 * i / static_cast<double>(I.d)));
-  hipError_t e = recsa::launch_rope_table(static_cast<float2*>(ws), P, static_cast<int>(I.d / 2), iv, st);
+  return iv;
+}
+
+int32_t fill_table(const Info& I, int64_t P, void* ws, hipStream_t st) {
+  if (I.theta == 0.0f) return RECSA_OK;
+  hipError_t e = recsa::launch_rope_table(static_cast<float2*>(ws), P, static_cast<int>(I.d / 2), inv_freq_of(I), st);
   if (e != hipSuccess) return hip_fail(e, "RoPE table launch");
+  return RECSA_OK;
+}
+
+// The table of positions 0..P from the device's RoPE table cache when it covers them (nullptr:
+// the call fills its own table in its workspace).
+int32_t cached_table(const Info& I, int64_t P, hipStream_t st, const float2** tab) {
+  *tab = nullptr;
+  if (I.theta == 0.0f) return RECSA_OK;
+  hipError_t e = recsa::rope_cache_table(static_cast<int>(I.d), I.theta, inv_freq_of(I), P, st, tab);
+  if (e != hipSuccess) return hip_fail(e, "RoPE table cache");
   return RECSA_OK;
 }
 
@@ -293,17 +307,28 @@ int32_t launch_planned_attend(const AttendPlan& pl, hipStream_t st) {
   return RECSA_OK;
 }
 
+// use_cache: take the RoPE table from the device's cache when it covers the call (the
+// allocation-free entry point always fills its own table in its scratch)
 int32_t run_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, const void* K, const void* V,
                    const void* tree, int64_t n_fixed, int64_t q_start, bool prefill, const int32_t* k,
                    int32_t n_levels, float* out, float* lse, int32_t* sel, int32_t sel_width, void* ws,
-                   int64_t ws_bytes, void* stream) {
+                   int64_t ws_bytes, void* stream, bool use_cache = true) {
   AttendPlan pl;
   int32_t rc = prepare_attend(shape, q, n_q, K, V, tree, n_fixed, q_start, prefill, k, n_levels, out, lse, sel,
                               sel_width, ws, ws_bytes, &pl);
   if (rc || pl.empty) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = fill_table(pl.I, pl.P, ws, st);
-  if (rc) return rc;
+  const float2* tab = nullptr;
+  if (use_cache) {
+    rc = cached_table(pl.I, pl.P, st, &tab);
+    if (rc) return rc;
+  }
+  if (tab) {
+    pl.a.tab = tab;
+  } else {
+    rc = fill_table(pl.I, pl.P, ws, st);
+    if (rc) return rc;
+  }
   return launch_planned_attend(pl, st);
 }
 
@@ -440,7 +465,7 @@ int32_t recsa_decode_noalloc(const recsa_shape_t* shape, const void* q, int64_t 
     if (e != hipSuccess) return hip_fail(e, "scratch address");
   }
   return run_attend(shape, q, n_q, K, V, tree, n_tokens, 0, false, k, n_levels, out, lse, sel, sel_width, scratch,
-                    have, stream);
+                    have, stream, false);
 }
 
 int32_t recsa_prefill(const recsa_shape_t* shape, const void* q, int64_t q_start, int64_t n_q, const void* K,
@@ -499,13 +524,19 @@ int32_t recsa_decode_step(const recsa_shape_t* shape, const void* q, const void*
   sa.f = static_cast<int32_t>(I.f);
   sa.BH = static_cast<int32_t>(I.B * I.Hkv);
   sa.half = static_cast<int32_t>(I.d / 2);
-  if (I.theta != 0.0f) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the RoPE table: from the device's cache when it covers the call (the append launch then has
+  // no table rows to fill), else filled into the workspace by the append launch's extra workgroups
+  const float2* cached = nullptr;
+  rc = cached_table(I, pl.P, st, &cached);
+  if (rc) return rc;
+  if (cached) {
+    pl.a.tab = cached;
+  } else if (I.theta != 0.0f) {
     sa.tab = static_cast<float2*>(workspace);
     sa.P = pl.P;
-    for (int i = 0; i < I.d / 2; ++i)
-      sa.iv.w[i] = static_cast<float>(std::pow(static_cast<double>(I.theta), -2.0 * i / static_cast<double>(I.d)));
+    sa.iv = inv_freq_of(I);
   }
-  hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = recsa::launch_append_step(sa, static_cast<int>(I.d), I.bf16, st);
   if (e != hipSuccess) return hip_fail(e, "append step launch");
   return launch_planned_attend(pl, st);
@@ -766,13 +797,6 @@ static DensePlan dense_plan(const Info& I, int64_t n_tokens, int64_t n_q, int32_
   }
   p.total = p.kr_bytes + p.qr_bytes + p.part_o_bytes + p.part_ml_bytes;
   return p;
-}
-
-static recsa::InvFreq inv_freq_of(const Info& I) {
-  recsa::InvFreq iv{};
-  for (int i = 0; i < I.d / 2; ++i)
-    iv.w[i] = static_cast<float>(std::pow(static_cast<double>(I.theta), -2.0 * i / static_cast<double>(I.d)));
-  return iv;
 }
 
 int64_t recsa_dense_workspace_bytes(const recsa_shape_t* shape, int64_t n_tokens, int64_t n_q, int32_t mode) {

@@ -273,4 +273,10 @@ hipError_t launch_ts_tokens(const TsArgs& a, int d, bool bf16, int G, size_t lds
 // (looked up once per device).
 hipError_t noalloc_scratch_address(void** out);
 
+// The RoPE table cache (rope_cache.hip): *tab = its device rows when this device's cache holds
+// (d, theta) and covers positions 0..P (filling it on `st` if no call has yet), else nullptr (the
+// caller fills its own table). Waits on `st` for a fill enqueued by another stream until that fill
+// is known to be complete; under graph capture only a completed cache is used.
+hipError_t rope_cache_table(int d, float theta, const InvFreq& iv, int64_t P, hipStream_t st, const float2** tab);
+
 }  // namespace recsa

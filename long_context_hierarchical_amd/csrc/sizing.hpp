@@ -63,4 +63,10 @@ __host__ __device__ inline int dense_queries_per_block(int G) { return 4 * (32 /
 // Bytes of the library's per-device scratch array: the RoPE table for up to 8191 positions at d = 128.
 constexpr size_t kNoallocScratchBytes = size_t(4) << 20;
 
+// ---------------------------------------------------------------- RoPE table cache
+// Rows (positions 0 .. kRopeCacheRows - 1) of the per-device RoPE table cache, for head sizes up
+// to kRopeCacheHeadDim: 4 MiB of (cos, sin) pairs.
+constexpr int64_t kRopeCacheRows = 8192;
+constexpr int kRopeCacheHeadDim = 128;
+
 }  // namespace recsa

@@ -37,6 +37,12 @@ hipError_t launch_ts_score(const TsArgs&, int, bool, int, hipStream_t) { return 
 hipError_t launch_ts_merge(const TsArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_ts_tokens(const TsArgs&, int, bool, int, size_t, int64_t, hipStream_t) { return hipSuccess; }
 
+// no device: the cache never holds a table, so every call takes the workspace path
+hipError_t rope_cache_table(int, float, const InvFreq&, int64_t, hipStream_t, const float2** tab) {
+  *tab = nullptr;
+  return hipSuccess;
+}
+
 alignas(256) static unsigned char fake_scratch[256];
 hipError_t noalloc_scratch_address(void** out) {
   *out = fake_scratch;

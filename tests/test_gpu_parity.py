@@ -99,8 +99,12 @@ def test_tree_build_bitwise(w):
                 assert np.array_equal(got_k, wk), f"keys differ at level {lv}: {np.sum(got_k != wk)} elements"
 
 
-def test_rope_table_bitwise():
-    """The (cos, sin) table the kernels read equals the oracle's bit for bit."""
+def test_rope_table_bitwise(monkeypatch):
+    """The (cos, sin) table the kernels read equals the oracle's bit for bit. With the library's
+    RoPE table cache turned off the call fills its table in its workspace, where it is read back;
+    the cache is filled by the same kernel (a row does not depend on the table's length), and
+    test_gpu_rope_cache checks that cached and uncached calls agree bit for bit."""
+    monkeypatch.setenv("RECSA_ROPE_CACHE", "0")
     w = _w("tab", Hq=32, Hkv=8, d=128, dtype="bf16", L=16 ** 4 + 100, f=16, k=8, n_queries=1, seed=6)
     inp = gen_decode_inputs(w, n_q=1, heads=[0])
     g = Gpu(w, inp)
