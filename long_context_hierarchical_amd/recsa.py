@@ -59,9 +59,14 @@ class Shape:
     select_heads: int = 0     # query heads per selection (0 = the KV head's group)
 
     def c(self) -> _Shape:
-        return _Shape(self.batch, self.n_kv_heads, self.n_q_heads, self.head_dim, self.fanout,
-                      RECSA_BF16 if self.dtype == "bf16" else RECSA_F32, self.capacity,
-                      self.softmax_scale, self.rope_theta, self.select_heads)
+        # the C struct, built once per (immutable) shape: a decoding loop passes it every step
+        st = self.__dict__.get("_c")
+        if st is None:
+            st = _Shape(self.batch, self.n_kv_heads, self.n_q_heads, self.head_dim, self.fanout,
+                        RECSA_BF16 if self.dtype == "bf16" else RECSA_F32, self.capacity,
+                        self.softmax_scale, self.rope_theta, self.select_heads)
+            object.__setattr__(self, "_c", st)
+        return st
 
     @property
     def torch_dtype(self):
@@ -115,17 +120,34 @@ def lib() -> ctypes.CDLL:
 
 
 def _p(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # the argument types are c_void_p: an int (or None = NULL) converts directly
+    return None if t is None else t.data_ptr()
+
+
+_K_ARRAYS: dict = {}
 
 
 def _k(k_levels):
-    k_levels = [int(x) for x in k_levels]
-    return (ctypes.c_int32 * max(len(k_levels), 1))(*k_levels), len(k_levels)
+    # the k_l array, built once per distinct tuple (the library reads it during the call only)
+    key = tuple(int(x) for x in k_levels)
+    hit = _K_ARRAYS.get(key)
+    if hit is None:
+        hit = ((ctypes.c_int32 * max(len(key), 1))(*key), len(key))
+        if len(_K_ARRAYS) < 1024:
+            _K_ARRAYS[key] = hit
+    return hit
+
+
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    # the HIP stream handle: the given stream's, else torch's current stream on the current device
+    if stream is not None:
+        return stream.cuda_stream
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _check(rc: int):
