@@ -308,17 +308,24 @@ def shared_level(n, f, k):
     return 0, 0
 
 
+def values_on_mfma(w):
+    """bf16 storage with at least two query heads per KV head: the weighted value sums run on the
+    matrix cores."""
+    return w.dtype == "bf16" and w.Hq // w.Hkv >= 2
+
+
 def valu_roofline(w, rows, n_queries, ms, mf_rows=0):
     """The attention kernel against the vector-ALU roofline (it is issue-bound; its row reads
     mostly hit the cache). Algorithmic work per query: one multiply-add per (query head, element)
     for every logit computed on the vector units (the scored rows, less the first scored level's
-    mf_rows, whose logits come from the matrix cores) and for every weighted value row; key
+    mf_rows, whose logits come from the matrix cores) and, when the value sums run on the vector
+    units (float32 storage, one query head per KV head), for every weighted value row; key
     rotation, selection and exponentials are not counted. Logits run on v_dot2_f32_bf16 (2
     multiply-adds per lane-instruction; v_fma_f32 for float32 storage), values on v_fma_f32 (1):
     the time at peak issue is logit_macs / (2 or 1) + value_macs lane-instructions over
     VALU_LANE_OPS, and `peak` is the flop rate that time implies for this mix."""
     logit_macs = w.d * w.Hq * (rows["key_rows"] + rows["tok_rows"] - mf_rows)
-    value_macs = w.d * w.Hq * (rows["val_rows"] + rows["tok_rows"])
+    value_macs = 0 if values_on_mfma(w) else w.d * w.Hq * (rows["val_rows"] + rows["tok_rows"])
     per_dot = 2 if w.dtype == "bf16" else 1
     t_peak = (logit_macs / per_dot + value_macs) / VALU_LANE_OPS * n_queries
     flops = 2 * (logit_macs + value_macs) * n_queries
@@ -329,14 +336,16 @@ def valu_roofline(w, rows, n_queries, ms, mf_rows=0):
             "peak_derivation": "256 CU x 4 SIMD x 2.4 GHz / 4 clk x 64 lanes; dot2 = 2 MAC, fma = 1 MAC"}
 
 
-def mfma_share(w, n_queries, ms, c_shared):
-    """The first scored level's logits on the matrix cores: 2 * d * H_q * C flops per query
-    (useful; rows past the workgroup's queries are not counted), as a rate over the whole call
-    and as a fraction of the 2.5 PFLOP/s bf16 peak."""
-    fl = 2.0 * w.d * w.Hq * c_shared * n_queries
-    ach = fl / (ms * 1e-3) / 1e12
-    return {"flops_per_call": fl, "candidates": c_shared, "achieved_over_call": round(ach, 2), "unit": "TFLOP/s",
-            "frac_of_peak_over_call": round(ach / 2500.0, 5)}
+def mfma_share(w, n_queries, ms, c_shared, rows):
+    """Useful matrix-core flops: the first scored level's logits, 2 * d * H_q * C per query (rows
+    past the workgroup's queries not counted), and, when they run there (values_on_mfma), the
+    weighted value sums, 2 * d * H_q per weighted row (each weight's two bf16 terms counted once);
+    as a rate over the whole call and as a fraction of the 2.5 PFLOP/s bf16 peak."""
+    tile = 2.0 * w.d * w.Hq * c_shared * n_queries
+    vals = 2.0 * w.d * w.Hq * (rows["val_rows"] + rows["tok_rows"]) * n_queries if values_on_mfma(w) else 0.0
+    ach = (tile + vals) / (ms * 1e-3) / 1e12
+    return {"flops_per_call": tile + vals, "tile_flops": tile, "value_flops": vals, "candidates": c_shared,
+            "achieved_over_call": round(ach, 2), "unit": "TFLOP/s", "frac_of_peak_over_call": round(ach / 2500.0, 5)}
 
 
 def needle_recall(w, sel, cpu):
@@ -430,9 +439,7 @@ def prefill_64k_leg(R, dev, timed, dense=True):
            "ms": round(ms, 4), "tokens_per_s": round(w.L / (ms * 1e-3), 1),
            "scored_rows": scored, "entries": entries,
            "roofline_alu": valu_roofline(w, rows, 1, ms, mf_rows=mf_rows),
-           "mfma_first_scored_level": {"flops": 2.0 * w.d * w.Hq * mf_rows,
-                                       "achieved_over_call": round(2.0 * w.d * w.Hq * mf_rows / (ms * 1e-3) / 1e12, 3),
-                                       "unit": "TFLOP/s"}}
+           "mfma": mfma_share(w, 1, ms, mf_rows, rows)}
     if dense:
         mode = R.RECSA_DENSE_CAUSAL
         dws = torch.empty(max(R.recsa_dense_workspace_bytes(sh, w.L, w.L, mode), 16), dtype=torch.uint8, device=dev)
@@ -806,7 +813,7 @@ def main():
             "build_bytes": bb, "tree_nodes_per_slice": n_nodes,
             "roofline_other": roof("attend_kernel" if dom == "pool_kernel" else "pool_kernel"),
             "decode_alu": valu_roofline(w, rows, n_queries, decode_ms, mf_rows=mf_c),
-            "decode_mfma_first_scored_level": mfma_share(w, n_queries, decode_ms, mf_c),
+            "decode_mfma": mfma_share(w, n_queries, decode_ms, mf_c, rows),
             "needle_recall": needle_recall(w, sel.cpu().numpy(), cpu),
             "hbm_probe": probe,
         },
@@ -862,7 +869,7 @@ def main():
                                             # a position within c of L scores and reads what a
                                             # query at L does
                                             "roofline_alu": valu_roofline(w, rows, w.B * c, ms, mf_rows=mf_c),
-                                            "mfma_first_scored_level": mfma_share(w, w.B * c, ms, mf_c)}
+                                            "mfma": mfma_share(w, w.B * c, ms, mf_c, rows)}
         psw = R.recsa_sel_width(sh, w.L - c + 1, w.L, k)
         psel = torch.empty(w.B, c, w.Hkv, len(k), psw, dtype=torch.int32, device=dev)
         R.recsa_prefill(sh, qp, w.L - c, K, V, tree, k, pout, None, psel, psw, pws)
