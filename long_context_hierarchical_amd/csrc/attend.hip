@@ -404,7 +404,7 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
   (void)args;
   const AttnArgs& a = *(const AttnArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
   constexpr int VE = 4;                // elements per row group lane (one wave), value phase
-  constexpr int VEW = VE / NW;         // elements per lane of each wave
+  constexpr int VEW = VE / NW > 0 ? VE / NW : 1;   // elements per lane of each wave (fmaf value path)
   constexpr int RL = D / VE;           // lanes per row, value phase
   constexpr int RPP = kWave / RL;      // rows per pass, value phase
   constexpr int SL = D / 16;           // lanes per row, score phase (8 rotate-half pairs per lane)
@@ -415,13 +415,16 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
   constexpr int SCPR = D * ESZ / 16;   // 16-byte pieces per row, staged value rows
   constexpr int SR = NW * kWave * 4 / SCPR;   // rows per staging round
   static_assert(NW == 1 || SR % (8 * (kWave / (D / VE))) == 0, "a staging round holds whole 8-row residue steps");
-  static_assert(VE % NW == 0, "waves split the value elements of a lane");
 
   // bf16 storage: the first level a unit scores holds every node of that level, in order, for
   // every unit of the workgroup; its logits come from one matrix-core tile (see mf_level below)
   constexpr bool MF = BF16;
   // bf16 storage with G >= 2: the value pass on the matrix cores (mv_read_tr above)
   constexpr bool MV = BF16 && G >= 2;
+  // the fmaf value path splits a lane's value elements between the waves (NW <= 4); the
+  // matrix-core one takes whole (head group, column block) pairs, so it runs with 8 waves too
+  static_assert(NW == 1 || NW == 4 || (MV && NW == 8), "waves per unit");
+  static_assert(MV || VE % NW == 0, "waves split the value elements of a lane");
   constexpr int HG = G > 4 ? G / 4 : 1;   // groups of 4 query heads
   constexpr int CB = D / 64;              // 64-column blocks of the value rows
   extern __shared__ __align__(16) unsigned char lds_all[];
@@ -1331,18 +1334,21 @@ static hipError_t launch_attend_t(const AttnArgs& a, size_t lds, int64_t B, hipS
     // to whole 8-row residue steps -- 8 * 64 / (D / 4) rows -- then to whole 64-lane loads of
     // 16 bytes), prefetched while the chunk is scored; else rounds of 4 waves x 64 lanes x 4
     // pieces of 16 bytes
+    // bf16 with G >= 2 (the value pass on the matrix cores): 8 waves per unit, whose score passes
+    // cover 64 candidate rows each (a level's 128 in two passes, both in flight at once); else 4
+    constexpr bool kMV = BF16 && G >= 2;
+    constexpr int kNW = kMV ? 8 : 4;
     constexpr size_t kPiecesPerRow = D * (BF16 ? 2 : 4) / 16;
     constexpr size_t kStep = 8 * kWave / (D / 4);
     const size_t rows = (static_cast<size_t>(a.zcap) + kStep - 1) / kStep * kStep;
     const size_t kFull = (rows * kPiecesPerRow + kWave - 1) / kWave * kWave * 16;
-    constexpr size_t kStage = 4 * kWave * 4 * 16;
-    hipError_t e = allow_full_lds<D, BF16, G, 4>();
+    constexpr size_t kStage = static_cast<size_t>(kNW) * kWave * 4 * 16;
+    hipError_t e = allow_full_lds<D, BF16, G, kNW>();
     if (e != hipSuccess) return e;
     // the staged value rows, then the tile's rows (the first scored level's value rows are
-    // requested before its tile is computed)
-    // bf16 with G >= 2: then the bf16 weights of the matrix-core value pass, which reads the
-    // value rows from LDS (a staging mode is always granted: a unit's LDS is at most 64 KB)
-    constexpr bool kMV = BF16 && G >= 2;
+    // requested before its tile is computed), then (matrix-core value pass) the bf16 weights;
+    // that pass reads the value rows from LDS, and a staging mode is always granted (a unit's
+    // LDS is at most 64 KB)
     const size_t pwb = kMV ? static_cast<size_t>(4 * G) * static_cast<size_t>(a.zcap) : 0;
     AttnArgs b = a;
     if (lds + kFull + mf + pwb <= kLdsMax) {
@@ -1356,7 +1362,7 @@ static hipError_t launch_attend_t(const AttnArgs& a, size_t lds, int64_t B, hipS
       b.pv_stage = 0;
       b.stage_bytes = 0;
     }
-    hipLaunchKernelGGL((attend_kernel<D, BF16, G, 4>), grid, dim3(4 * kWave), lds + b.stage_bytes + mf + pwb, s, b);
+    hipLaunchKernelGGL((attend_kernel<D, BF16, G, kNW>), grid, dim3(kNW * kWave), lds + b.stage_bytes + mf + pwb, s, b);
   } else {
     // bf16: up to 8 units of one KV head per workgroup, one wave each, whose rows fill the 32
     // rows of the first scored level's tile, as many as LDS holds; float32: one unit
