@@ -137,8 +137,9 @@ int32_t recsa_build_tree(const recsa_shape_t* shape, const void* K, const void* 
  *   l in row l-1, ascending, padded with -1; sel_width >= recsa_sel_width(n_tokens, n_tokens);
  *   groups = H_q / select_heads (H_kv by default).
  *   workspace [dev]: ws_bytes >= recsa_workspace_bytes(shape, n_tokens, k, n_levels).
- * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED (candidate lists too long for on-chip memory),
- * WORKSPACE. */
+ * Errors: INVALID_ARG, CAPACITY, UNSUPPORTED (candidate lists too long for on-chip memory, or
+ * a slice of capacity * head_dim elements -- or its RoPE table -- of 4 GiB or more: the kernels
+ * address a slice with 32-bit byte offsets), WORKSPACE. */
 int32_t recsa_decode(const recsa_shape_t* shape, const void* q, int64_t n_q,
                      const void* K, const void* V, const void* tree, int64_t n_tokens,
                      const int32_t* k_per_level, int32_t n_levels,

@@ -35,6 +35,7 @@ int32_t hip_fail(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxList = 4096;     // kept-node / candidate list capacity in LDS
+constexpr int64_t kMaxSliceBytes = int64_t(1) << 32;   // attention: 32-bit offsets within a slice
 constexpr size_t kMaxLds = 65536;
 constexpr size_t kMaxLdsMerge = 163840;   // gfx950: 160 KB of LDS per workgroup
 constexpr int64_t kTableAlign = 256;
@@ -253,6 +254,10 @@ int32_t prepare_attend(const recsa_shape_t* shape, const void* q, int64_t n_q, c
   if (bd.smax > kMaxList || bd.csel > kMaxList)
     return fail(RECSA_ERR_UNSUPPORTED, "candidate lists up to %lld entries exceed %lld", (long long)std::max(bd.smax, bd.csel),
                 (long long)kMaxList);
+  // the attention kernels address a slice's rows (one sequence and KV head of the caches or of a
+  // tree level) and the RoPE table with 32-bit byte offsets
+  if (I.cap * I.d * I.esz >= kMaxSliceBytes || table_bytes(I, bd.P) >= kMaxSliceBytes)
+    return fail(RECSA_ERR_UNSUPPORTED, "a cache slice of %lld tokens (or its RoPE table) reaches 4 GiB", (long long)I.cap);
   // scored-candidate buffers: every selecting level fits whole; the token level is processed in
   // chunks of zcap candidates, so an unbounded token list (no pruning) takes chunks of 256
   const int64_t zneed = std::max<int64_t>(bd.csel, std::min<int64_t>(bd.c0, 256));

@@ -142,6 +142,18 @@ __device__ __forceinline__ Raw8<BF16> raw8_load(const void* base, int64_t off) {
   return r;
 }
 
+// The same from a wave-uniform byte base and a 32-bit byte offset (the host keeps every slice of
+// the caches, the tree and the RoPE table under 4 GiB), so that the load takes its base from
+// scalar registers and one 32-bit add per address.
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> raw8_load32(const char* base, uint32_t boff) {
+  Raw8<BF16> r;
+  const uint4* p = reinterpret_cast<const uint4*>(base + boff);
+  r.u[0] = p[0];
+  if constexpr (!BF16) r.u[1] = p[1];
+  return r;
+}
+
 template <bool BF16>
 __device__ __forceinline__ Raw8<BF16> raw8_zero() {
   Raw8<BF16> r;
@@ -695,13 +707,17 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
     // one pass ahead; one wave fetches them at the start of the pass (fewer registers)
     constexpr bool PT = ROPE && NW > 1;
     float4 ta[PT ? 4 : 1], tb[PT ? 4 : 1];
+    // the slice's rows from a wave-uniform base: a row's byte offset fits 32 bits
+    const char* sbase = static_cast<const char*>(src) + rowbase * (D * ESZ);
+    const char* tbase = reinterpret_cast<const char*>(a.tab);
     auto fetch = [&](int32_t r0, Raw8<BF16>& lo, Raw8<BF16>& hi, float4 (&tn)[PT ? 4 : 1]) {
       const int32_t r = r0 + srg < cn ? r0 + srg : cn - 1;
-      const int64_t off = (rowbase + cid[r]) * D + 8 * ssub;
-      lo = raw8_load<BF16>(src, off);
-      hi = raw8_load<BF16>(src, off + HALF);
+      const uint32_t boff = static_cast<uint32_t>(cid[r]) * (D * ESZ) + static_cast<uint32_t>(8 * ssub * ESZ);
+      lo = raw8_load32<BF16>(sbase, boff);
+      hi = raw8_load32<BF16>(sbase, boff + HALF * ESZ);
       if constexpr (PT) {
-        const float4* t = reinterpret_cast<const float4*>(a.tab + static_cast<int64_t>(c0 + r) * HALF + 8 * ssub);
+        const uint32_t toff = (static_cast<uint32_t>(c0 + r) * HALF + 8 * ssub) * static_cast<uint32_t>(sizeof(float2));
+        const float4* t = reinterpret_cast<const float4*>(tbase + toff);
 #pragma unroll
         for (int u = 0; u < 4; ++u) tn[u] = t[u];
       }
@@ -712,7 +728,8 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
       const bool valid = r < cn;
       float4 tv[4];
       if constexpr (ROPE && !PT) {
-        const float4* t = reinterpret_cast<const float4*>(a.tab + static_cast<int64_t>(c0 + (valid ? r : 0)) * HALF + 8 * ssub);
+        const uint32_t toff = (static_cast<uint32_t>(c0 + (valid ? r : 0)) * HALF + 8 * ssub) * static_cast<uint32_t>(sizeof(float2));
+        const float4* t = reinterpret_cast<const float4*>(tbase + toff);
 #pragma unroll
         for (int u = 0; u < 4; ++u) tv[u] = t[u];
       }
@@ -786,8 +803,9 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
         sc[r] = S;
       }
     };
-    // the chunk's candidate -> row map, read by the row loads, the selection and the values
-    for (int32_t r = tid; r < cn; r += NT) cid[r] = cm(c0 + r);
+    // the chunk's candidate -> row map, read by the row loads, the selection and the values;
+    // entries up to the next multiple of 16 repeat the last candidate's row
+    for (int32_t r = tid; r < ((cn + 15) & ~15); r += NT) cid[r] = cm(c0 + (r < cn ? r : cn - 1));
     bsync();
     if (prefetched) prefetch_values(vsrc, rowbase, cn);
     Raw8<BF16> alo, ahi, blo, bhi;
@@ -814,6 +832,7 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
       for (int hh = 0; hh < G; ++hh) S = S + z[hh];
       sc[r] = S;
     }
+    for (int32_t r = cn + tid; r < ((cn + 15) & ~15); r += NT) cid[r] = cm(cn - 1);   // padding, as score_rows
     bsync();
     (void)vsrc;
     (void)rowbase;   // several waves: its value rows were requested before the tile
@@ -1123,13 +1142,19 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
       // weights are 0 (padded to a multiple of 16 rows), like the kept rows'.
       using RT = typename std::conditional<D == 128, uint32_t, uint16_t>::type;
       static_assert(D * 2 == 64 * static_cast<int>(sizeof(RT)), "a row is 64 units of RT");
-      const RT* vb = static_cast<const RT*>(vsrc) + rowbase * 64 + lane;
+      const char* vb = static_cast<const char*>(vsrc) + rowbase * (D * 2);   // wave-uniform
+      const uint32_t lane_off = static_cast<uint32_t>(lane) * static_cast<uint32_t>(sizeof(RT));
+      // the row ids of 8 rows in two 16-byte LDS reads (the map is padded to a multiple of 16 rows
+      // with the last candidate's row; a group past the padding re-reads the last 8)
+      const int32_t cn16 = (cn + 15) & ~15;
       auto gfetch = [&](int32_t r0, RT (&raw)[8]) {
+        const int32_t rc = r0 < cn16 - 8 ? r0 : cn16 - 8;
+        const int4 ca = *reinterpret_cast<const int4*>(cid + rc);
+        const int4 cb4 = *reinterpret_cast<const int4*>(cid + rc + 4);
+        const int32_t ids[8] = {ca.x, ca.y, ca.z, ca.w, cb4.x, cb4.y, cb4.z, cb4.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int32_t r = r0 + e;
-          raw[e] = vb[static_cast<int64_t>(cid[r < cn ? r : cn - 1]) * 64];
-        }
+        for (int e = 0; e < 8; ++e)
+          raw[e] = *reinterpret_cast<const RT*>(vb + static_cast<uint32_t>(ids[e]) * (D * 2) + lane_off);
       };
       auto gcompute = [&](int32_t r0, const RT (&raw)[8]) {
 #pragma unroll
@@ -1139,8 +1164,9 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
           for (int t = 0; t < 2; ++t) {
             const uint32_t x = raw[4 * qq + 2 * t], y = raw[4 * qq + 2 * t + 1];
             if constexpr (D == 128) {
-              w[0][t] = (x & 0xFFFFu) | (y << 16);
-              w[CB - 1][t] = (x >> 16) | (y & 0xFFFF0000u);
+              // one byte permute each: (x.lo, y.lo) and (x.hi, y.hi)
+              w[0][t] = __builtin_amdgcn_perm(y, x, 0x05040100u);
+              w[CB - 1][t] = __builtin_amdgcn_perm(y, x, 0x07060302u);
             } else {
               w[0][t] = x | (y << 16);
             }
