@@ -124,6 +124,28 @@ int main() {
                       nullptr, 0, fake(8), 1 << 20, nullptr) == RECSA_ERR_INVALID_ARG, "levels", 0);
   expect(recsa_decode(&sh, fake(1), 2, fake(2), fake(3), fake(4), 4096, k3, 3, static_cast<float*>(fake(5)), nullptr,
                       nullptr, 0, fake(8), 16, nullptr) == RECSA_ERR_WORKSPACE, "workspace", 0);
+  // a slice (one sequence and KV head) of 4 GiB or more: the attention kernels' 32-bit offsets
+  // would not reach it, so decode, prefill, the decoding step and the allocation-free decode
+  // refuse it; one row less is accepted
+  for (int dt = 0; dt < 2; ++dt) {
+    const int64_t big = (int64_t(1) << 32) / (128 * (dt == RECSA_BF16 ? 2 : 4));
+    for (int64_t cap : {big, big - 1}) {
+      recsa_shape_t s4{1, 8, 32, 128, 16, dt, cap, 0.0f, 1.0e6f, 0};
+      const int32_t want = cap == big ? RECSA_ERR_UNSUPPORTED : RECSA_OK;
+      const int64_t ws4 = recsa_workspace_bytes(&s4, 4096, k3, 3);
+      expect(recsa_decode(&s4, fake(1), 2, fake(2), fake(3), fake(4), 4096, k3, 3, static_cast<float*>(fake(5)),
+                          nullptr, nullptr, 0, fake(8), ws4 > 0 ? ws4 : 16, nullptr) == want, "4 GiB decode", cap);
+      expect(recsa_prefill(&s4, fake(1), 4090, 6, fake(2), fake(3), fake(4), k3, 3, static_cast<float*>(fake(5)),
+                           nullptr, nullptr, 0, fake(8), ws4 > 0 ? ws4 : 16, nullptr) == want, "4 GiB prefill", cap);
+      expect(recsa_decode_noalloc(&s4, fake(1), 2, fake(2), fake(3), fake(4), 4096, k3, 3,
+                                  static_cast<float*>(fake(5)), nullptr, nullptr, 0, nullptr) == want,
+             "4 GiB decode_noalloc", cap);
+      expect(recsa_decode_step(&s4, fake(1), fake(20), fake(21), fake(2), fake(3), fake(9), fake(4), 4095, k3, 3,
+                               static_cast<float*>(fake(5)), nullptr, nullptr, 0, fake(8), ws4 > 0 ? ws4 : 16,
+                               nullptr) == want,
+             "4 GiB decode_step", cap);
+    }
+  }
   recsa_shape_t bad = sh;
   bad.n_q_heads = 30;
   expect(recsa_tree_bytes(&bad) == -1, "bad heads", 0);
