@@ -1144,21 +1144,24 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
       static_assert(D * 2 == 64 * static_cast<int>(sizeof(RT)), "a row is 64 units of RT");
       const char* vb = static_cast<const char*>(vsrc) + rowbase * (D * 2);   // wave-uniform
       const uint32_t lane_off = static_cast<uint32_t>(lane) * static_cast<uint32_t>(sizeof(RT));
-      // the row ids of 8 rows in two 16-byte LDS reads (the map is padded to a multiple of 16 rows
-      // with the last candidate's row; a group past the padding re-reads the last 8)
+      // the row ids of a group of VG rows in 16-byte LDS reads (the map is padded to a multiple of
+      // 16 rows with the last candidate's row; a group past the padding re-reads the last VG)
+      constexpr int VG = G <= 4 ? 16 : 8;   // 8 at G = 8 (registers)
       const int32_t cn16 = (cn + 15) & ~15;
-      auto gfetch = [&](int32_t r0, RT (&raw)[8]) {
-        const int32_t rc = r0 < cn16 - 8 ? r0 : cn16 - 8;
-        const int4 ca = *reinterpret_cast<const int4*>(cid + rc);
-        const int4 cb4 = *reinterpret_cast<const int4*>(cid + rc + 4);
-        const int32_t ids[8] = {ca.x, ca.y, ca.z, ca.w, cb4.x, cb4.y, cb4.z, cb4.w};
+      auto gfetch = [&](int32_t r0, RT (&raw)[VG]) {
+        const int32_t rc = r0 < cn16 - VG ? r0 : cn16 - VG;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          raw[e] = *reinterpret_cast<const RT*>(vb + static_cast<uint32_t>(ids[e]) * (D * 2) + lane_off);
+        for (int i = 0; i < VG / 4; ++i) {
+          const int4 c4 = *reinterpret_cast<const int4*>(cid + rc + 4 * i);
+          const int32_t ids[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            raw[4 * i + e] = *reinterpret_cast<const RT*>(vb + static_cast<uint32_t>(ids[e]) * (D * 2) + lane_off);
+        }
       };
-      auto gcompute = [&](int32_t r0, const RT (&raw)[8]) {
+      auto gcompute = [&](int32_t r0, const RT (&raw)[VG]) {
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
+        for (int qq = 0; qq < VG / 4; ++qq) {
           uint32_t w[CB][2];
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
@@ -1174,13 +1177,16 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
           mv_quad((r0 >> 2) + qq, [&](int cb) { return __builtin_bit_cast(mv_i16x4_t, make_uint2(w[cb][0], w[cb][1])); });
         }
       };
-      RT ra[8], rb[8];
+      // groups of VG rows (the quads up to the padded count, as the several-wave path takes them),
+      // the next group's rows in flight during this group's products
+      RT ra[VG], rb[VG];
       gfetch(0, ra);
-      for (int32_t r0 = 0; r0 < cn; r0 += 16) {
-        gfetch(r0 + 8, rb);
+      for (int32_t r0 = 0; r0 < cn; r0 += 2 * VG) {
+        gfetch(r0 + VG, rb);
         gcompute(r0, ra);
-        gfetch(r0 + 16, ra);
-        gcompute(r0 + 8, rb);
+        if (r0 + VG >= cn16) break;
+        gfetch(r0 + 2 * VG, ra);
+        gcompute(r0 + VG, rb);
       }
       bsync();
       return;
