@@ -403,6 +403,12 @@ int32_t recsa_build_tree(const recsa_shape_t* shape, const void* K, const void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int Tc = levels_of(I.cap, I.f);
   const bool can_fuse = recsa::pool_nodes_per_tile(static_cast<int>(I.d)) % I.f == 0;
+  // every launch of this call takes the one-tile form when the first (the largest) has at most
+  // one tile per CU: a short build is latency-bound. Otherwise every launch is persistent.
+  const int64_t npw = recsa::pool_nodes_per_tile(static_cast<int>(I.d));
+  const int64_t first_span = nodes_at(n_new, I.f, 1) - nodes_at(n_old, I.f, 1) / npw * npw;
+  const int64_t first_tiles = (first_span + npw - 1) / npw * I.B * I.Hkv;
+  const int32_t one_tile = first_tiles * 2 <= recsa::pool_persistent_grid() ? 1 : 0;
   for (int lv = 1; lv <= T;) {
     const int64_t lo = nodes_at(n_old, I.f, lv), hi = nodes_at(n_new, I.f, lv);
     const bool fuse = can_fuse && lv + 1 <= Tc;
@@ -425,6 +431,7 @@ int32_t recsa_build_tree(const recsa_shape_t* shape, const void* K, const void* 
       p.g_hi = hi;
       p.f = static_cast<int32_t>(I.f);
       p.BH = static_cast<int32_t>(I.B * I.Hkv);
+      p.one_tile = one_tile;
       if (fuse) {
         p.fuse_next = 1;
         p.dst2K = static_cast<char*>(tree) + level_offset_bytes(I, lv + 1, 0);

@@ -29,8 +29,16 @@ struct PoolArgs {
   void* dst2V;
   int64_t dst2_rows;
   int32_t grid;         // persistent grid size (0 = library default)
+  int32_t one_tile;     // 1: one 1024-thread workgroup per tile (pool_tile_kernel); 0: persistent
+  // Tile queue: with sched set, a workgroup's first tile is its index and each later one comes
+  // from an atomic counter that reads sched_base at the launch's start (tiles in the order
+  // workgroups ask for them); null: tiles blockIdx.x, + gridDim.x, ...
+  unsigned long long* sched;
+  unsigned long long sched_base;
 };
 hipError_t launch_pool_level(const PoolArgs& a, int d, bool bf16, hipStream_t s);
+// workgroups of the persistent build grid (two per CU)
+int pool_persistent_grid();
 
 // ---------------------------------------------------------------- RoPE table
 struct InvFreq {

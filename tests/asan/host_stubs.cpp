@@ -7,6 +7,7 @@
 namespace recsa {
 
 hipError_t launch_pool_level(const PoolArgs&, int, bool, hipStream_t) { return hipSuccess; }
+int pool_persistent_grid() { return 512; }
 hipError_t launch_rope_table(float2*, int64_t, int, const InvFreq&, hipStream_t) { return hipSuccess; }
 hipError_t launch_append_step(const StepArgs&, int, bool, hipStream_t) { return hipSuccess; }
 hipError_t launch_attend(const AttnArgs& a, int, bool, int, size_t, int64_t, hipStream_t) {
