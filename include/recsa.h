@@ -121,6 +121,11 @@ int64_t recsa_workspace_bytes(const recsa_shape_t* shape, int64_t n_max,
  * n_old are left untouched, so growing the cache in any number of steps gives the same tree.
  *   K, V [dev]: [B][H_kv][capacity][d] pre-RoPE; W [dev]: [d][d] (key_i = sum_j W[i][j] m_j);
  *   tree [dev]: recsa_tree_bytes(shape) bytes.
+ * Builds of different trees may run at once on different streams and may be captured in a HIP
+ * graph. Large launches hand their tiles out through one of a few device-resident counters, each
+ * serving one launch at a time (a launch that finds none free, or runs under graph capture, or
+ * with RECSA_BUILD_QUEUE=0 in the environment, takes its tiles in a fixed order); the nodes do
+ * not depend on the order. Allocates nothing.
  * Errors: INVALID_ARG (null, misaligned, n_old > n_new, n_old < 0), CAPACITY (n_new > capacity),
  * UNSUPPORTED (d, f or dtype). */
 int32_t recsa_build_tree(const recsa_shape_t* shape, const void* K, const void* V, const void* W,
