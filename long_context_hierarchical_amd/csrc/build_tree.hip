@@ -566,14 +566,14 @@ __global__ __launch_bounds__(1024) void pool_tile_kernel(PoolArgs a) {
 static_assert(PoolGeom<128>::NPW == 32 && PoolGeom<64>::NPW == 64, "pool_nodes_per_tile (sizing.hpp)");
 
 int pool_persistent_grid() {
-  static int cus = 0;
-  if (cus == 0) {
+  // the first call's device's CU count (initialised once, also when host threads call at once)
+  static const int cus = [] {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
+      return n;
+    (void)hipGetLastError();
+    return 256;
+  }();
   return 2 * cus;  // two 512-thread workgroups fit a CU's LDS
 }
 

@@ -197,3 +197,42 @@ def test_small_launches_build_the_one_shot_tree(shape):
         R.recsa_build_tree(sh, K, V, W, a, b, inc)
     torch.cuda.synchronize()
     _same(_levels(sh, inc, L, f), _levels(sh, one, L, f), "4096-token increments")
+
+
+def test_builds_from_several_host_threads():
+    """Four host threads, each building its own tree on its own stream six times (the library
+    call releases the interpreter lock, so the calls overlap on the host and on the GPU): every
+    tree equals the static-order tree."""
+    import threading
+    B, Hkv, d, dtype, f, L = 1, 8, 128, "bf16", 16, 16 ** 4 + 16 ** 2 * 7 + 5
+    _say("build queue: 4 host threads")
+    K, V, W = _inputs(B, Hkv, d, dtype, L, seed=51)
+    sh = R.Shape(B, Hkv, 32, d, f, dtype, L, 0.0, 1.0e6)
+    ref = _tree(sh)
+    with _queue(False):
+        R.recsa_build_tree(sh, K, V, W, 0, L, ref)
+    torch.cuda.synchronize()
+    want = _levels(sh, ref, L, f)
+    trees = [_tree(sh) for _ in range(4)]
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        try:
+            for _ in range(6):
+                R.recsa_build_tree(sh, K, V, W, 0, L, trees[i], stream=streams[i])
+            streams[i].synchronize()
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    with _queue(True):
+        threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, t in enumerate(trees):
+        _same(_levels(sh, t, L, f), want, f"thread {i}")
