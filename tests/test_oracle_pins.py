@@ -728,12 +728,16 @@ def test_replay_with_imposed_sets_matches_brute_force(seed):
     the float64 brute force with the same set imposed: the levels below, the entries and the
     outputs. The imposed set is the lowest-scoring s candidates, so it differs from the natural
     choice."""
-    f, d, G, theta, self_in, n, k, K, V, q, W = _brute_case(seed + 100)
-    tree = build_slice(K, V, W, f, "f32", n_new=n)
-    r = attend_unit(q, K, V, tree, n, f, k, "f32", theta, self_in=self_in)
-    lv = next((lv for lv in sorted(r.scores, reverse=True) if 0 < len(r.sel[lv]) < len(r.scores[lv][0])), None)
-    if lv is None:
-        pytest.skip("no level selects a strict subset")
+    # the case: the first of seed + 100, seed + 116, ... with a level that keeps a strict subset
+    # of its candidates (a random tiny tree need not have one)
+    for case in range(seed + 100, seed + 100 + 16 * 32, 16):
+        f, d, G, theta, self_in, n, k, K, V, q, W = _brute_case(case)
+        tree = build_slice(K, V, W, f, "f32", n_new=n)
+        r = attend_unit(q, K, V, tree, n, f, k, "f32", theta, self_in=self_in)
+        lv = next((lv for lv in sorted(r.scores, reverse=True) if 0 < len(r.sel[lv]) < len(r.scores[lv][0])), None)
+        if lv is not None:
+            break
+    assert lv is not None, "no case with a level that keeps a strict subset"
     cand, S = r.scores[lv]
     s = len(r.sel[lv])
     worst = sorted(int(c) for c in cand[np.lexsort((-np.arange(len(S)), S))][:s])
