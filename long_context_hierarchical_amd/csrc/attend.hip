@@ -793,14 +793,18 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) part[hh] = lane_group_sum<SL>(part[hh]);
       if (valid && ssub == 0) {
-        float S = 0.0f, z[G];
+        if constexpr (NW == 1) {
+          zrow_store(r, part);   // scaled, and summed into the group score, after the passes
+        } else {
+          float S = 0.0f, z[G];
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          z[hh] = part[hh] * a.scale;
-          S = S + z[hh];
+          for (int hh = 0; hh < G; ++hh) {
+            z[hh] = part[hh] * a.scale;
+            S = S + z[hh];
+          }
+          zrow_store(r, z);
+          sc[r] = S;
         }
-        zrow_store(r, z);
-        sc[r] = S;
       }
     };
     // the chunk's candidate -> row map, read by the row loads, the selection and the values;
@@ -816,6 +820,22 @@ __global__ __launch_bounds__(NW == 1 && BF16 ? 512 : 64 * NW) __attribute__((amd
       pass(r0, alo, ahi, ta, blo, bhi, tb);
       if (r0 + NW * SPP >= cn) break;
       pass(r0 + NW * SPP, blo, bhi, tb, alo, ahi, ta);
+    }
+    if constexpr (NW == 1) {
+      // one wave: the logits z = scale * dot and the group score S = sum of the G logits in
+      // head order, one candidate per lane (the same arithmetic as the several-wave passes)
+      wave_sync();
+      for (int32_t r = lane; r < cn; r += kWave) {
+        float z[G], S = 0.0f;
+        zrow_load(r, z);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          z[hh] = z[hh] * a.scale;
+          S = S + z[hh];
+        }
+        zrow_store(r, z);
+        sc[r] = S;
+      }
     }
     bsync();
   };

@@ -22,9 +22,12 @@ __device__ __forceinline__ void wave_sync() {
 // Sum over each group of N (4, 8 or 16) consecutive lanes, left in every lane of the group, with
 // DPP lane moves (no LDS round trip): pairs of lanes, pairs of pairs, then (N = 8) the two
 // quads of the half-row, mirrored, then (N = 16) the two halves of the row, mirrored.
+// Every control used here moves lanes within one 16-lane row, so no source lane is out of
+// bounds: bound_ctrl (an out-of-bounds source reads 0) changes no result, and it lets the
+// compiler drop the move's zero-initialised destination.
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 template <int N>
