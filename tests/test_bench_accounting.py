@@ -40,3 +40,16 @@ def test_unique_rows_match_the_oracle_union(L, f, k, nq):
     rows = sum(map(len, keys.values())) + sum(map(len, vals.values())) + 2 * sum(map(len, toks.values()))
     w = SimpleNamespace(f=f, L=L, d=d, elem_bytes=4)
     assert bench.decode_unique_bytes(w, k, sel) == rows * d * 4
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """--gpus above 1 ends with a message and exit status 2 before any GPU work."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
