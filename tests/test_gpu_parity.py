@@ -208,6 +208,11 @@ ONE_WAVE_CASES = [
     (_w("w1_bf16_d128_G8_f32", Hq=16, Hkv=2, d=128, dtype="bf16", L=40000, f=32, k=16, n_queries=1030, seed=43),
      [16] * 3),
     (_w("w1_f32_d128_G4_f16", Hq=8, Hkv=2, d=128, dtype="f32", L=5000, k=8, n_queries=1030, seed=44), [8] * 3),
+    # bf16 without the rotation (the unrotated score passes next to the matrix-core tile)
+    (_w("w1_bf16_d128_G4_norope", Hq=8, Hkv=2, d=128, dtype="bf16", L=5000, k=8, n_queries=1030, theta=0.0,
+        seed=45), [8] * 3),
+    # bf16 with one query head per KV head (the tile, then the fmaf value sums)
+    (_w("w1_bf16_d128_G1_f16", Hq=2, Hkv=2, d=128, dtype="bf16", L=6000, k=8, n_queries=1030, seed=46), [8] * 3),
 ]
 
 
@@ -382,10 +387,12 @@ TIE_CASES = [
 
 
 @pytest.mark.parametrize("case", TIE_CASES, ids=lambda c: f"{c[0]}_{c[1]}_d{c[2]}_G{c[3]}_f{c[4]}")
-@pytest.mark.parametrize("mode", ["decode", "prefill"])
+@pytest.mark.parametrize("mode", ["decode", "prefill", "prefill_wide"])
 def test_exact_ties_keep_lowest_indices(case, mode):
     """Equal group scores at the k-th place: the kept sets must be exactly the oracle's (equal
-    scores go to the lower candidate index); no near-tie allowance applies to exact ties."""
+    scores go to the lower candidate index); no near-tie allowance applies to exact ties.
+    decode and prefill (300 positions) run a few waves per unit; prefill_wide (1100 positions x 2
+    KV heads, over 2048 units) one wave per unit."""
     kind, dtype, d, G, f, L, k = case
     Hkv, n_q = 2, 4
     w = _w(f"tie_{kind}", B=1, Hq=G * Hkv, Hkv=Hkv, d=d, dtype=dtype, L=L, f=f, k=k[0], n_queries=n_q,
@@ -399,9 +406,10 @@ def test_exact_ties_keep_lowest_indices(case, mode):
         units = [(0, j, h) for j in range(n_q) for h in range(Hkv)]
         ref = oracle.decode(inp["K"], inp["V"], inp["W"], inp["q"], L, f, kk, dtype, w.theta, units=units)
     else:
-        q_start = L - 300
-        res = g.prefill(kk, q_start, 300)
-        pos = [0, 1, 2, 15, 16, 17, 100, 255, 256, 299]
+        n_p = 1100 if mode == "prefill_wide" else 300
+        q_start = L - n_p
+        res = g.prefill(kk, q_start, n_p)
+        pos = [0, 1, 2, 15, 16, 17, 100, 255, 256, 299] + ([640, 1023, 1099] if n_p > 300 else [])
         units = [(0, p, h) for p in pos for h in range(Hkv)]
         ref = oracle.prefill(inp["K"], inp["V"], inp["W"], inp["q"][:, q_start:], q_start, f, kk, dtype, w.theta,
                              units=units)
